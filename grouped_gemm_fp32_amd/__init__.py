@@ -1,0 +1,277 @@
+"""Python binding of libmoe.so, the gfx950 MoE feed-forward path of dots.llm1 (include/moe.h).
+
+Argument marshalling only: every function here passes device pointers of torch tensors (PyTorch
+provides device memory and streams) to the C entry point of the same name, which does all the work
+in HIP kernels. Nothing falls back to a CPU path: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "MoeShape", "MoeError", "load_library", "library_path", "declared_functions",
+    "MOE_NORM_TOPK", "MOE_PROBS_IN", "MOE_FWD_GATEUP", "MOE_FWD_DOWN", "MOE_FWD",
+    "MOE_DGRAD_DOWN", "MOE_DGRAD_GATEUP", "MOE_WGRAD_DOWN", "MOE_WGRAD_GATEUP", "MOE_DGRAD",
+    "MOE_WGRAD",
+    "moe_abi_version", "moe_status_string", "moe_last_error", "moe_row_capacity",
+    "moe_workspace_size", "moe_route", "moe_permute", "grouped_gemm_fwd", "grouped_gemm_bwd",
+    "moe_combine", "moe_combine_bwd", "moe_unpermute_bwd", "make_shape", "alloc_buffers",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
+
+MOE_NORM_TOPK = 0x1
+MOE_PROBS_IN = 0x2
+MOE_FWD_GATEUP, MOE_FWD_DOWN = 0x1, 0x2
+MOE_FWD = MOE_FWD_GATEUP | MOE_FWD_DOWN
+MOE_DGRAD_DOWN, MOE_DGRAD_GATEUP, MOE_WGRAD_DOWN, MOE_WGRAD_GATEUP = 0x1, 0x2, 0x4, 0x8
+MOE_DGRAD = MOE_DGRAD_DOWN | MOE_DGRAD_GATEUP
+MOE_WGRAD = MOE_WGRAD_DOWN | MOE_WGRAD_GATEUP
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("I", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("block_m", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+    @property
+    def G(self):
+        return self.E + self.S
+
+    def __repr__(self):
+        return ("MoeShape(T=%d, H=%d, E=%d, K=%d, I=%d, S=%d, block_m=%d, flags=%#x)"
+                % (self.T, self.H, self.E, self.K, self.I, self.S, self.block_m, self.flags))
+
+
+def make_shape(T, H, E, K, I, S, block_m, flags=MOE_NORM_TOPK) -> MoeShape:
+    return MoeShape(T, H, E, K, I, S, block_m, flags)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: {status} ({msg})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("MOE_LIB", os.path.join(_PKG, "libmoe.so"))
+
+
+_lib = None
+_P = ctypes.c_void_p
+_SP = ctypes.POINTER(MoeShape)
+_SIGS = {
+    "moe_abi_version": (ctypes.c_int32, []),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_row_capacity": (ctypes.c_int64, [_SP]),
+    "moe_workspace_size": (ctypes.c_size_t, [_SP]),
+    "moe_route": (ctypes.c_int, [_SP] + [_P] * 10),
+    "moe_permute": (ctypes.c_int, [_SP] + [_P] * 9 + [ctypes.c_size_t, _P]),
+    "grouped_gemm_fwd": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 10),
+    "grouped_gemm_bwd": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 14),
+    "moe_combine": (ctypes.c_int, [_SP] + [_P] * 6),
+    "moe_combine_bwd": (ctypes.c_int, [_SP] + [_P] * 10),
+    "moe_unpermute_bwd": (ctypes.c_int, [_SP] + [_P] * 5),
+}
+
+
+def load_library():
+    """Load libmoe.so once. Raises if it is missing: there is no fallback implementation."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m grouped_gemm_fp32_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(lib, name)
+            f.restype, f.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def declared_functions() -> list:
+    """Function names declared in include/moe.h."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+|grouped_gemm_\w+)\s*\(", text)))
+
+
+# ------------------------------------------------------------------------------------------------
+# marshalling helpers
+# ------------------------------------------------------------------------------------------------
+def _ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    dev = next((t.device for t in tensors if hasattr(t, "device")), None)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(fn, status):
+    if status != 0:
+        lib = load_library()
+        raise MoeError(fn, lib.moe_status_string(status).decode(), lib.moe_last_error().decode())
+
+
+def _bf16():
+    import torch
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _i32():
+    import torch
+    return (torch.int32,)
+
+
+# ------------------------------------------------------------------------------------------------
+# entry points (same names and argument order as include/moe.h)
+# ------------------------------------------------------------------------------------------------
+def moe_abi_version() -> int:
+    return load_library().moe_abi_version()
+
+
+def moe_status_string(status: int) -> str:
+    return load_library().moe_status_string(status).decode()
+
+
+def moe_last_error() -> str:
+    return load_library().moe_last_error().decode()
+
+
+def moe_row_capacity(shape: MoeShape) -> int:
+    return int(load_library().moe_row_capacity(ctypes.byref(shape)))
+
+
+def moe_workspace_size(shape: MoeShape) -> int:
+    return int(load_library().moe_workspace_size(ctypes.byref(shape)))
+
+
+def moe_route(shape, x, w_gate, logit_bias, sel_bias, logits, probs, topk_idx, topk_w,
+              expert_counts, stream=None):
+    lib = load_library()
+    st = _stream(stream, topk_idx)
+    _check("moe_route", lib.moe_route(
+        ctypes.byref(shape), _ptr(x, "x", _bf16()), _ptr(w_gate, "w_gate", _f32()),
+        _ptr(logit_bias, "logit_bias", _f32()), _ptr(sel_bias, "sel_bias", _f32()),
+        _ptr(logits, "logits", _f32()), _ptr(probs, "probs", _f32()),
+        _ptr(topk_idx, "topk_idx", _i32()), _ptr(topk_w, "topk_w", _f32()),
+        _ptr(expert_counts, "expert_counts", _i32()), st))
+
+
+def moe_permute(shape, topk_idx, x, seg_offsets, tile_group, total_rows, row_token, pos, x_perm,
+                ws, stream=None):
+    lib = load_library()
+    st = _stream(stream, topk_idx)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("moe_permute", lib.moe_permute(
+        ctypes.byref(shape), _ptr(topk_idx, "topk_idx", _i32()), _ptr(x, "x", _bf16()),
+        _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(tile_group, "tile_group", _i32()),
+        _ptr(total_rows, "total_rows", _i32()), _ptr(row_token, "row_token", _i32()),
+        _ptr(pos, "pos", _i32()), _ptr(x_perm, "x_perm", _bf16()), _ptr(ws, "ws"), ws_bytes, st))
+
+
+def grouped_gemm_fwd(shape, which, x_perm, seg_offsets, tile_group, total_rows, w1, w2, h_save, a,
+                     y_perm, stream=None):
+    lib = load_library()
+    st = _stream(stream, a)
+    _check("grouped_gemm_fwd", lib.grouped_gemm_fwd(
+        ctypes.byref(shape), which, _ptr(x_perm, "x_perm", _bf16()),
+        _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(tile_group, "tile_group", _i32()),
+        _ptr(total_rows, "total_rows", _i32()), _ptr(w1, "w1", _bf16()), _ptr(w2, "w2", _bf16()),
+        _ptr(h_save, "h_save", _bf16()), _ptr(a, "a", _bf16()), _ptr(y_perm, "y_perm", _bf16()),
+        st))
+
+
+def grouped_gemm_bwd(shape, which, x_perm, h_save, a, dy_perm, seg_offsets, tile_group, total_rows,
+                     w1, w2, dh, dx_perm, dw1, dw2, stream=None):
+    lib = load_library()
+    st = _stream(stream, dw1, dh)
+    _check("grouped_gemm_bwd", lib.grouped_gemm_bwd(
+        ctypes.byref(shape), which, _ptr(x_perm, "x_perm", _bf16()), _ptr(h_save, "h_save", _bf16()),
+        _ptr(a, "a", _bf16()), _ptr(dy_perm, "dy_perm", _bf16()),
+        _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(tile_group, "tile_group", _i32()),
+        _ptr(total_rows, "total_rows", _i32()), _ptr(w1, "w1", _bf16()), _ptr(w2, "w2", _bf16()),
+        _ptr(dh, "dh", _bf16()), _ptr(dx_perm, "dx_perm", _bf16()), _ptr(dw1, "dw1", _bf16()),
+        _ptr(dw2, "dw2", _bf16()), st))
+
+
+def moe_combine(shape, y_perm, pos, topk_w, seg_offsets, y, stream=None):
+    lib = load_library()
+    st = _stream(stream, y_perm)
+    _check("moe_combine", lib.moe_combine(
+        ctypes.byref(shape), _ptr(y_perm, "y_perm", _bf16()), _ptr(pos, "pos", _i32()),
+        _ptr(topk_w, "topk_w", _f32()), _ptr(seg_offsets, "seg_offsets", _i32()),
+        _ptr(y, "y", _bf16()), st))
+
+
+def moe_combine_bwd(shape, dy, y_perm, pos, topk_w, seg_offsets, row_token, total_rows, dy_perm,
+                    dtopk_w, stream=None):
+    lib = load_library()
+    st = _stream(stream, dy)
+    _check("moe_combine_bwd", lib.moe_combine_bwd(
+        ctypes.byref(shape), _ptr(dy, "dy", _bf16()), _ptr(y_perm, "y_perm", _bf16()),
+        _ptr(pos, "pos", _i32()), _ptr(topk_w, "topk_w", _f32()),
+        _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(row_token, "row_token", _i32()),
+        _ptr(total_rows, "total_rows", _i32()), _ptr(dy_perm, "dy_perm", _bf16()),
+        _ptr(dtopk_w, "dtopk_w", _f32()), st))
+
+
+def moe_unpermute_bwd(shape, dx_perm, pos, seg_offsets, dx, stream=None):
+    lib = load_library()
+    st = _stream(stream, dx_perm)
+    _check("moe_unpermute_bwd", lib.moe_unpermute_bwd(
+        ctypes.byref(shape), _ptr(dx_perm, "dx_perm", _bf16()), _ptr(pos, "pos", _i32()),
+        _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(dx, "dx", _bf16()), st))
+
+
+# ------------------------------------------------------------------------------------------------
+# device buffers (torch allocations sized by the capacity query)
+# ------------------------------------------------------------------------------------------------
+def alloc_buffers(shape: MoeShape, device, backward: bool = False, save_h: bool = True) -> dict:
+    """Every buffer the forward (and optionally backward) calls write, on `device`."""
+    import torch
+    T, H, E, K, I, G, B = shape.T, shape.H, shape.E, shape.K, shape.I, shape.G, shape.block_m
+    mcap = moe_row_capacity(shape)
+    if mcap < 0:
+        raise MoeError("moe_row_capacity", "MOE_ERR_INVALID_ARG", repr(shape))
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    e = lambda *s, dtype=bf: torch.empty(*s, dtype=dtype, device=device)  # noqa: E731
+    buf = dict(
+        mcap=mcap,
+        logits=e(T, E, dtype=f32), probs=e(T, E, dtype=f32),
+        topk_idx=e(T, K, dtype=i32), topk_w=e(T, K, dtype=f32), expert_counts=e(E, dtype=i32),
+        seg_offsets=e(G + 1, dtype=i32), tile_group=e(max(1, mcap // B), dtype=i32),
+        total_rows=e(1, dtype=i32), row_token=e(max(1, mcap), dtype=i32), pos=e(T, K, dtype=i32),
+        ws=e(max(1, moe_workspace_size(shape)), dtype=torch.uint8),
+        x_perm=e(mcap, H), a=e(mcap, I), y_perm=e(mcap, H), y=e(T, H),
+        h_save=e(mcap, 2 * I) if (save_h or backward) else None,
+    )
+    if backward:
+        buf.update(dy_perm=e(mcap, H), dtopk_w=e(T, K, dtype=f32), dh=e(mcap, 2 * I),
+                   dx_perm=e(mcap, H), dx=e(T, H), dw1=e(G, 2 * I, H), dw2=e(G, H, I))
+    return buf

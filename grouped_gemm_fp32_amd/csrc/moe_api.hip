@@ -1,0 +1,290 @@
+// C ABI of the MoE feed-forward path (declared in include/moe.h): host-side argument checks,
+// then launches on the caller's stream. No allocation, no synchronisation, no global state.
+#include <stdio.h>
+#include <string.h>
+
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+void set_err(const char* what) {
+  snprintf(g_err, sizeof(g_err), "%s", what);
+}
+
+moe_status_t hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MOE_OK;
+  snprintf(g_err, sizeof(g_err), "%s: %s", where, hipGetErrorString(e));
+  return MOE_ERR_HIP;
+}
+
+constexpr int kMaxT = 262144;
+
+// Shape checks shared by every entry point. Returns MOE_OK or the failure code.
+moe_status_t check_shape(const moe_shape_t* s) {
+  if (!s) { set_err("shape is NULL"); return MOE_ERR_INVALID_ARG; }
+  if (s->T < 0 || s->H <= 0 || s->E <= 0 || s->K < 1 || s->K > s->E || s->I <= 0 || s->S < 0 ||
+      s->block_m <= 0) {
+    set_err("invalid shape (need T>=0, H,E,I>0, 1<=K<=E, S>=0, block_m>0)");
+    return MOE_ERR_INVALID_ARG;
+  }
+  const int b = s->block_m;
+  if (!(b == 16 || b == 32 || b == 64 || b == 128 || b == 256)) {
+    set_err("block_m must be one of 16, 32, 64, 128, 256");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (s->H % 128 != 0 || s->I % 64 != 0) {
+    set_err("need H % 128 == 0 and I % 64 == 0");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (s->E > 256 || s->K > 8 || s->S > 4 || s->T > kMaxT) {
+    set_err("need E <= 256, K <= 8, S <= 4, T <= 262144");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (s->flags & ~(uint32_t)(MOE_NORM_TOPK | MOE_PROBS_IN)) {
+    set_err("unknown flag bits");
+    return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+int64_t capacity(const moe_shape_t* s) {
+  const int64_t T = s->T, B = s->block_m;
+  const int64_t R = T * s->K;
+  int64_t routed = (R + (int64_t)s->E * (B - 1)) / B;
+  if (routed > R) routed = R;
+  return B * (routed + (int64_t)s->S * ((T + B - 1) / B));
+}
+
+#define REQUIRE(p)                                                \
+  do {                                                            \
+    if (!(p)) {                                                   \
+      set_err("required pointer is NULL: " #p);                   \
+      return MOE_ERR_INVALID_ARG;                                 \
+    }                                                             \
+  } while (0)
+
+#define CHECK_SHAPE(s)                       \
+  do {                                       \
+    moe_status_t st_ = check_shape(s);       \
+    if (st_ != MOE_OK) return st_;           \
+    g_err[0] = 0;                            \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int64_t moe_row_capacity(const moe_shape_t* s) {
+  if (check_shape(s) != MOE_OK) return -1;
+  return capacity(s);
+}
+
+size_t moe_workspace_size(const moe_shape_t* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return sizeof(int32_t) * (size_t)moe::permute_num_blocks(s->T) * (size_t)s->E;
+}
+
+moe_status_t moe_route(const moe_shape_t* s, const uint16_t* x, const float* w_gate,
+                       const float* logit_bias, const float* sel_bias, float* logits, float* probs,
+                       int32_t* topk_idx, float* topk_w, int32_t* expert_counts, void* stream) {
+  CHECK_SHAPE(s);
+  if (s->T == 0) return MOE_OK;
+  REQUIRE(topk_idx);
+  REQUIRE(topk_w);
+  if (s->flags & MOE_PROBS_IN) {
+    REQUIRE(probs);
+  } else if (x) {
+    REQUIRE(w_gate);
+  } else {
+    REQUIRE(logits);
+  }
+  return hip_status(moe::launch_route(*s, x, w_gate, logit_bias, sel_bias, logits, probs, topk_idx,
+                                      topk_w, expert_counts, (hipStream_t)stream),
+                    "moe_route");
+}
+
+moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx, const uint16_t* x,
+                         int32_t* seg_offsets, int32_t* tile_group, int32_t* total_rows,
+                         int32_t* row_token, int32_t* pos, uint16_t* x_perm, void* ws,
+                         size_t ws_bytes, void* stream) {
+  CHECK_SHAPE(s);
+  REQUIRE(seg_offsets);
+  REQUIRE(total_rows);
+  if (s->T == 0) {
+    // Still define the (empty) segments so later calls see G+1 zero offsets and no rows.
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = moe::launch_fill_i32(seg_offsets, 0, s->E + s->S + 1, st);
+    if (e == hipSuccess) e = moe::launch_fill_i32(total_rows, 0, 1, st);
+    return hip_status(e, "moe_permute");
+  }
+  REQUIRE(topk_idx);
+  REQUIRE(tile_group);
+  REQUIRE(row_token);
+  REQUIRE(pos);
+  if (x) REQUIRE(x_perm);
+  REQUIRE(ws);
+  if (ws_bytes < moe_workspace_size(s)) {
+    set_err("workspace smaller than moe_workspace_size()");
+    return MOE_ERR_WORKSPACE;
+  }
+  return hip_status(moe::launch_permute(*s, capacity(s), topk_idx, x, seg_offsets, tile_group,
+                                        total_rows, row_token, pos, x_perm, (int32_t*)ws,
+                                        (hipStream_t)stream),
+                    "moe_permute");
+}
+
+moe_status_t grouped_gemm_fwd(const moe_shape_t* s, uint32_t which, const uint16_t* x_perm,
+                              const int32_t* seg_offsets, const int32_t* tile_group,
+                              const int32_t* total_rows, const uint16_t* w1, const uint16_t* w2,
+                              uint16_t* h_save, uint16_t* a, uint16_t* y_perm, void* stream) {
+  CHECK_SHAPE(s);
+  if (which == 0 || (which & ~(uint32_t)MOE_FWD)) {
+    set_err("which must be a non-empty combination of MOE_FWD_GATEUP and MOE_FWD_DOWN");
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (s->T == 0) return MOE_OK;
+  REQUIRE(seg_offsets);
+  REQUIRE(tile_group);
+  REQUIRE(total_rows);
+  REQUIRE(a);
+  if (which & MOE_FWD_GATEUP) {
+    REQUIRE(x_perm);
+    REQUIRE(w1);
+  }
+  if (which & MOE_FWD_DOWN) {
+    REQUIRE(w2);
+    REQUIRE(y_perm);
+  }
+  return hip_status(moe::launch_ggemm_fwd(*s, which, capacity(s), x_perm, tile_group, total_rows,
+                                          w1, w2, h_save, a, y_perm, (hipStream_t)stream),
+                    "grouped_gemm_fwd");
+}
+
+moe_status_t grouped_gemm_bwd(const moe_shape_t* s, uint32_t which, const uint16_t* x_perm,
+                              const uint16_t* h_save, const uint16_t* a, const uint16_t* dy_perm,
+                              const int32_t* seg_offsets, const int32_t* tile_group,
+                              const int32_t* total_rows, const uint16_t* w1, const uint16_t* w2,
+                              uint16_t* dh, uint16_t* dx_perm, uint16_t* dw1, uint16_t* dw2,
+                              void* stream) {
+  CHECK_SHAPE(s);
+  if (which == 0 || (which & ~(uint32_t)(MOE_DGRAD | MOE_WGRAD))) {
+    set_err("which must be a non-empty combination of the MOE_DGRAD_* and MOE_WGRAD_* bits");
+    return MOE_ERR_INVALID_ARG;
+  }
+  const bool rows = s->T > 0;  // with T == 0 no activation row is read and dgrad is a no-op
+  if (rows && (which & MOE_DGRAD)) {
+    REQUIRE(tile_group);
+    REQUIRE(total_rows);
+    REQUIRE(dh);
+  }
+  if (rows && (which & MOE_DGRAD_DOWN)) {
+    REQUIRE(dy_perm);
+    REQUIRE(h_save);
+    REQUIRE(w2);
+  }
+  if (rows && (which & MOE_DGRAD_GATEUP)) {
+    REQUIRE(w1);
+    REQUIRE(dx_perm);
+  }
+  if (which & MOE_WGRAD) REQUIRE(seg_offsets);
+  if (which & MOE_WGRAD_DOWN) {
+    REQUIRE(dw2);
+    if (rows) {
+      REQUIRE(dy_perm);
+      REQUIRE(a);
+    }
+  }
+  if (which & MOE_WGRAD_GATEUP) {
+    REQUIRE(dw1);
+    if (rows) {
+      REQUIRE(dh);
+      REQUIRE(x_perm);
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (rows && (which & MOE_DGRAD)) {
+    moe_status_t r = hip_status(moe::launch_ggemm_dgrad(*s, which, capacity(s), dy_perm, h_save,
+                                                        tile_group, total_rows, w1, w2, dh,
+                                                        dx_perm, st),
+                                "grouped_gemm_bwd(dgrad)");
+    if (r != MOE_OK) return r;
+  }
+  if (which & MOE_WGRAD) {
+    return hip_status(moe::launch_ggemm_wgrad(*s, which, x_perm, a, dy_perm, dh, seg_offsets, dw1,
+                                              dw2, st),
+                      "grouped_gemm_bwd(wgrad)");
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_combine(const moe_shape_t* s, const uint16_t* y_perm, const int32_t* pos,
+                         const float* topk_w, const int32_t* seg_offsets, uint16_t* y,
+                         void* stream) {
+  CHECK_SHAPE(s);
+  if (s->T == 0) return MOE_OK;
+  REQUIRE(y_perm);
+  REQUIRE(pos);
+  REQUIRE(topk_w);
+  REQUIRE(seg_offsets);
+  REQUIRE(y);
+  if (s->T == 0) return MOE_OK;
+  return hip_status(moe::launch_combine(*s, y_perm, pos, topk_w, seg_offsets, y,
+                                        (hipStream_t)stream),
+                    "moe_combine");
+}
+
+moe_status_t moe_combine_bwd(const moe_shape_t* s, const uint16_t* dy, const uint16_t* y_perm,
+                             const int32_t* pos, const float* topk_w, const int32_t* seg_offsets,
+                             const int32_t* row_token, const int32_t* total_rows,
+                             uint16_t* dy_perm, float* dtopk_w, void* stream) {
+  CHECK_SHAPE(s);
+  if (s->T == 0) return MOE_OK;
+  REQUIRE(dy);
+  REQUIRE(y_perm);
+  REQUIRE(pos);
+  REQUIRE(topk_w);
+  REQUIRE(seg_offsets);
+  REQUIRE(row_token);
+  REQUIRE(total_rows);
+  REQUIRE(dy_perm);
+  REQUIRE(dtopk_w);
+  if (s->T == 0) return MOE_OK;
+  return hip_status(moe::launch_combine_bwd(*s, capacity(s), dy, y_perm, pos, topk_w, seg_offsets,
+                                            row_token, total_rows, dy_perm, dtopk_w,
+                                            (hipStream_t)stream),
+                    "moe_combine_bwd");
+}
+
+moe_status_t moe_unpermute_bwd(const moe_shape_t* s, const uint16_t* dx_perm, const int32_t* pos,
+                               const int32_t* seg_offsets, uint16_t* dx, void* stream) {
+  CHECK_SHAPE(s);
+  if (s->T == 0) return MOE_OK;
+  REQUIRE(dx_perm);
+  REQUIRE(pos);
+  REQUIRE(seg_offsets);
+  REQUIRE(dx);
+  if (s->T == 0) return MOE_OK;
+  return hip_status(moe::launch_unpermute_bwd(*s, dx_perm, pos, seg_offsets, dx,
+                                              (hipStream_t)stream),
+                    "moe_unpermute_bwd");
+}
+
+}  // extern "C"

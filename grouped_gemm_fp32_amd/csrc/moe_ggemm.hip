@@ -1,0 +1,491 @@
+// Grouped GEMM engine of the MoE expert FFN on gfx950 (bf16 MFMA, fp32 accumulation).
+//
+// dots.llm1 Technical Report, section 3.2 "Efficient grouped GEMM": every expert's token segment
+// is padded to a fixed block size that is a multiple of the matrix instruction's M, so all rows of
+// a workgroup tile belong to one expert and the grouped GEMM is scheduled like an ordinary GEMM.
+// Section A2 (MoE paragraph): each expert is a two-layer FFN with SwiGLU.
+//
+// On gfx950 the instruction is v_mfma_f32_32x32x16_bf16 (or 16x16x32 for 16-row tiles); the
+// workgroup tile is BM x BN x 64 with BM dividing block_m, four wavefronts, and both operands
+// staged through LDS as K-contiguous rows (operands stored the other way round in HBM are
+// transposed 8x8 in registers on the way in). Tiles are ordered so that consecutive ones share
+// an M-block (and an expert), and mapped to XCDs so that they also share an L2.
+//
+// Six kinds of tile share the engine:
+//   FwdGateUp   h = x_perm . W1[g]^T, fused a = silu(h_gate) * h_up (and h_save)
+//   FwdDown     y_perm = a . W2[g]^T
+//   DgradDown   da = dy_perm . W2[g], fused SwiGLU backward -> dh
+//   DgradGateUp dx_perm = dh . W1[g]
+//   WgradDown   dW2[g] = dy_perm_seg^T . a_seg        (contraction over the segment's rows)
+//   WgradGateUp dW1[g] = dh_seg^T . x_perm_seg
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBK = 64;              // k per LDS stage
+constexpr int kLdk = kBK + 8;        // padded LDS row (bf16 elements): 144 bytes, conflict-light
+constexpr int kThreads = 256;
+
+enum Kind { kFwdGateUp, kFwdDown, kDgradDown, kDgradGateUp, kWgradDown, kWgradGateUp };
+
+template <int KIND> struct KindTraits {
+  static constexpr bool a_trans = KIND == kWgradDown || KIND == kWgradGateUp;
+  static constexpr bool b_trans = KIND != kFwdGateUp && KIND != kFwdDown;
+  static constexpr bool split = KIND == kFwdGateUp;      // B rows: [gate half | up half]
+  static constexpr bool grouped_rows = !a_trans;         // rows come from segments
+};
+
+struct GemmArgs {
+  const uint16_t* a;   // A source
+  const uint16_t* b;   // B source
+  int64_t lda, ldb;
+  int64_t b_gstride;   // elements per group of the B source (weights); 0 for wgrad
+  const uint16_t* aux; // h_save read by the SwiGLU backward epilogue
+  uint16_t* out;
+  int64_t ldo;
+  int64_t o_gstride;   // elements per group of the output (wgrad)
+  uint16_t* out2;      // h_save written by the forward gate/up epilogue (may be null)
+  int M, N, K, I;
+  int block_m;
+  int n_tiles_n, n_tiles_m;
+  int G;
+  const int32_t* tile_group;
+  const int32_t* total_rows;
+  const int32_t* seg;
+};
+
+template <int MS> struct Mfma;
+template <> struct Mfma<32> {
+  typedef f32x16_t acc_t;
+  static constexpr int regs = 16, ksub = 16;
+  __device__ static acc_t run(bf16x8_t a, bf16x8_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // Lane's operand row and k offset inside a sub-step.
+  __device__ static int row(int lane) { return lane & 31; }
+  __device__ static int kofs(int lane) { return (lane >> 5) * 8; }
+  // Output: lane -> column m (the second operand's row), register r -> first-operand row n.
+  __device__ static int out_m(int lane) { return lane & 31; }
+  __device__ static int out_n(int lane, int q) { return 8 * q + 4 * (lane >> 5); }  // + (r & 3)
+  static constexpr int groups = 4;  // groups of 4 consecutive n per lane
+};
+template <> struct Mfma<16> {
+  typedef f32x4_t acc_t;
+  static constexpr int regs = 4, ksub = 32;
+  __device__ static acc_t run(bf16x8_t a, bf16x8_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static int row(int lane) { return lane & 15; }
+  __device__ static int kofs(int lane) { return (lane >> 4) * 8; }
+  __device__ static int out_m(int lane) { return lane & 15; }
+  __device__ static int out_n(int lane, int q) { return 4 * (lane >> 4); }
+  static constexpr int groups = 1;
+};
+
+// 8x8 transpose of bf16: in[k] holds 8 consecutive m at k; out[m] holds 8 consecutive k at m.
+__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(in);  // w[k*4 + m/2], half m%2
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);             // o[m*4 + k/2], half k%2
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      const uint32_t lo = w[(2 * kp) * 4 + (m >> 1)], hi = w[(2 * kp + 1) * 4 + (m >> 1)];
+      o[m * 4 + kp] = (m & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Operand staging. Each loader fetches one BK-slab of ROWS operand rows from HBM into registers
+// (load) and writes it to LDS as [ROWS][kLdk] K-contiguous rows (store).
+// ------------------------------------------------------------------------------------------------
+
+// K-contiguous source: element (r, k) at base + row_ofs(r) + k. ROWS*8 16-byte chunks.
+template <int ROWS> struct LoaderK {
+  static constexpr int kChunks = ROWS * 8;
+  static constexpr int kIters = (kChunks + kThreads - 1) / kThreads;
+  uint4 v[kIters];
+  template <class RowPtr>
+  __device__ void load(RowPtr rowptr, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int idx = tid + i * kThreads;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (kChunks % kThreads == 0 || idx < kChunks) {
+        const uint16_t* p = rowptr(idx >> 3);
+        if (p) v[i] = *reinterpret_cast<const uint4*>(p + k0 + (idx & 7) * 8);
+      }
+    }
+  }
+  __device__ void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int idx = tid + i * kThreads;
+      if (kChunks % kThreads == 0 || idx < kChunks)
+        *reinterpret_cast<uint4*>(lds + (idx >> 3) * kLdk + (idx & 7) * 8) = v[i];
+    }
+  }
+};
+
+// Row-contiguous source ([K][rows] in HBM): element (r, k) at base + k*ld + r. Each thread takes
+// 8x8 blocks: 8 loads of 8 rows at consecutive k, transposed in registers, 8 LDS row writes.
+template <int ROWS> struct LoaderT {
+  static constexpr int kBlocks = (ROWS / 8) * (kBK / 8);
+  static constexpr int kIters = (kBlocks + kThreads - 1) / kThreads;
+  uint4 v[kIters][8];
+  // base points at (k = 0, r = 0) of the slab; rows >= rlim and k >= klim read as zero.
+  __device__ void load(const uint16_t* base, int64_t ld, int rlim, int klim, int tid) {
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int b = tid + i * kThreads;
+      const int rb = b % (ROWS / 8), kb = b / (ROWS / 8);
+      const bool ok = (kBlocks % kThreads == 0 || b < kBlocks) && rb * 8 < rlim;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int k = kb * 8 + q;
+        v[i][q] = make_uint4(0, 0, 0, 0);
+        if (ok && k < klim) v[i][q] = *reinterpret_cast<const uint4*>(base + (int64_t)k * ld + rb * 8);
+      }
+    }
+  }
+  __device__ void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int b = tid + i * kThreads;
+      if (kBlocks % kThreads == 0 || b < kBlocks) {
+        const int rb = b % (ROWS / 8), kb = b / (ROWS / 8);
+        uint4 t[8];
+        transpose8x8(v[i], t);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+          *reinterpret_cast<uint4*>(lds + (rb * 8 + m) * kLdk + kb * 8) = t[m];
+      }
+    }
+  }
+};
+
+template <bool TRANS, int ROWS> struct LoaderSel { typedef LoaderK<ROWS> type; };
+template <int ROWS> struct LoaderSel<true, ROWS> { typedef LoaderT<ROWS> type; };
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+
+template <int KIND, int BM, int BN, int MS, int WAVES_M>
+__global__ __launch_bounds__(kThreads, 2) void ggemm_kernel(GemmArgs p) {
+  typedef KindTraits<KIND> Tr;
+  typedef Mfma<MS> Mf;
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int TM = WTM / MS, TN = WTN / MS;
+  static_assert(TM >= 1 && TN >= 1 && WTM % MS == 0 && WTN % MS == 0, "tile shape");
+  static_assert(!Tr::split || TN % 2 == 0, "split needs gate/up pairs");
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[BM * kLdk];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b[BN * kLdk];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+  // ---- tile decode ------------------------------------------------------------------------------
+  int g, m0, n0, kbeg, klen;
+  if (Tr::grouped_rows) {
+    const int total = p.total_rows[0];
+    const int64_t n_valid = (int64_t)(total / BM) * p.n_tiles_n;
+    const int64_t L = xcd_remap(blockIdx.x, n_valid);
+    if (L < 0) return;
+    const int mt = (int)(L / p.n_tiles_n), nt = (int)(L % p.n_tiles_n);
+    m0 = mt * BM;
+    n0 = nt * (Tr::split ? BN / 2 : BN);
+    g = p.tile_group[m0 / p.block_m];
+    kbeg = 0;
+    klen = p.K;
+  } else {
+    const int64_t per_g = (int64_t)p.n_tiles_m * p.n_tiles_n;
+    const int64_t L = xcd_remap(blockIdx.x, per_g * p.G);
+    if (L < 0) return;
+    g = (int)(L / per_g);
+    const int rem = (int)(L % per_g);
+    m0 = (rem / p.n_tiles_n) * BM;
+    n0 = (rem % p.n_tiles_n) * BN;
+    kbeg = p.seg[g];
+    klen = p.seg[g + 1] - kbeg;
+  }
+
+  typename Mf::acc_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < Mf::regs; ++r) acc[i][j][r] = 0.0f;
+
+  typename LoaderSel<Tr::a_trans, BM>::type la;
+  typename LoaderSel<Tr::b_trans, BN>::type lb;
+
+  // Row pointers of K-contiguous operands (k offset added by the loader).
+  const uint16_t* a_rows = p.a + (int64_t)m0 * p.lda;
+  const uint16_t* b_grp = p.b + (int64_t)g * p.b_gstride;
+  auto a_row = [&](int r) -> const uint16_t* { return a_rows + (int64_t)r * p.lda; };
+  auto b_row = [&](int r) -> const uint16_t* {
+    if (Tr::split) {
+      const int half = BN / 2;
+      const int c = n0 + (r % half);
+      if (c >= p.I) return nullptr;
+      return b_grp + (int64_t)((r < half ? 0 : p.I) + c) * p.ldb;
+    }
+    if (n0 + r >= p.N) return nullptr;
+    return b_grp + (int64_t)(n0 + r) * p.ldb;
+  };
+
+  auto load_stage = [&](int k0) {
+    if constexpr (Tr::a_trans) {
+      la.load(p.a + (int64_t)(kbeg + k0) * p.lda + m0, p.lda, p.M - m0, klen - k0, tid);
+    } else {
+      la.load(a_row, k0, tid);
+    }
+    if constexpr (Tr::b_trans) {
+      lb.load(b_grp + (int64_t)(kbeg + k0) * p.ldb + n0, p.ldb, p.N - n0, klen - k0, tid);
+    } else {
+      lb.load(b_row, k0, tid);
+    }
+  };
+
+  // LDS row of the wave's B sub-tile j.
+  auto b_lds_row = [&](int j) {
+    if (Tr::split) {
+      constexpr int half = TN / 2;
+      return (j / half) * (BN / 2) + wn * (WTN / 2) + (j % half) * MS;
+    }
+    return wn * WTN + j * MS;
+  };
+
+  const int nk = (klen + kBK - 1) / kBK;
+  if (nk > 0) {
+    load_stage(0);
+    la.store(lds_a, tid);
+    lb.store(lds_b, tid);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load_stage((kt + 1) * kBK);
+#pragma unroll
+    for (int ks = 0; ks < kBK; ks += Mf::ksub) {
+      bf16x8_t af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(
+            lds_a + (wm * WTM + i * MS + Mf::row(lane)) * kLdk + ks + Mf::kofs(lane));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8_t*>(
+            lds_b + (b_lds_row(j) + Mf::row(lane)) * kLdk + ks + Mf::kofs(lane));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = Mf::run(bf[j], af[i], acc[i][j]);
+    }
+    __syncthreads();
+    if (kt + 1 < nk) {
+      la.store(lds_a, tid);
+      lb.store(lds_b, tid);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds row m = m_in, registers hold 4 consecutive columns per group --------
+  const int m_in = Mf::out_m(lane);
+  if constexpr (Tr::split) {
+    constexpr int half = TN / 2;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + wm * WTM + i * MS + m_in;
+#pragma unroll
+      for (int jj = 0; jj < half; ++jj)
+#pragma unroll
+        for (int q = 0; q < Mf::groups; ++q) {
+          const int c = n0 + wn * (WTN / 2) + jj * MS + Mf::out_n(lane, q);
+          if (c >= p.I) continue;
+          float av[4];
+          uint32_t hg[2], hu[2];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gv = acc[i][jj][4 * q + e], uv = acc[i][jj + half][4 * q + e];
+            av[e] = silu_f(gv) * uv;
+          }
+          hg[0] = pack_bf2(acc[i][jj][4 * q], acc[i][jj][4 * q + 1]);
+          hg[1] = pack_bf2(acc[i][jj][4 * q + 2], acc[i][jj][4 * q + 3]);
+          hu[0] = pack_bf2(acc[i][jj + half][4 * q], acc[i][jj + half][4 * q + 1]);
+          hu[1] = pack_bf2(acc[i][jj + half][4 * q + 2], acc[i][jj + half][4 * q + 3]);
+          *reinterpret_cast<uint2*>(p.out + m * p.ldo + c) =
+              make_uint2(pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3]));
+          if (p.out2) {
+            *reinterpret_cast<uint2*>(p.out2 + m * (2 * (int64_t)p.I) + c) = make_uint2(hg[0], hg[1]);
+            *reinterpret_cast<uint2*>(p.out2 + m * (2 * (int64_t)p.I) + p.I + c) =
+                make_uint2(hu[0], hu[1]);
+          }
+        }
+    }
+  } else {
+    uint16_t* out = p.out + (Tr::grouped_rows ? 0 : (int64_t)g * p.o_gstride);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int mloc = wm * WTM + i * MS + m_in;
+      const int64_t m = m0 + mloc;
+      if (!Tr::grouped_rows && m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < Mf::groups; ++q) {
+          const int c = n0 + wn * WTN + j * MS + Mf::out_n(lane, q);
+          if (c >= p.N) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+          if constexpr (KIND == kDgradDown) {
+            // da -> dh = [da*u*s*(1 + g(1-s)) | da*g*s] with g, u from h_save (bf16).
+            const int64_t hrow = m * (2 * (int64_t)p.I);
+            const uint2 gw = *reinterpret_cast<const uint2*>(p.aux + hrow + c);
+            const uint2 uw = *reinterpret_cast<const uint2*>(p.aux + hrow + p.I + c);
+            const float gg[4] = {lo_bf(gw.x), hi_bf(gw.x), lo_bf(gw.y), hi_bf(gw.y)};
+            const float uu[4] = {lo_bf(uw.x), hi_bf(uw.x), lo_bf(uw.y), hi_bf(uw.y)};
+            float dg[4], du[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float s = 1.0f / (1.0f + expf(-gg[e]));
+              dg[e] = v[e] * uu[e] * s * (1.0f + gg[e] * (1.0f - s));
+              du[e] = v[e] * gg[e] * s;
+            }
+            *reinterpret_cast<uint2*>(p.out + hrow + c) =
+                make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(p.out + hrow + p.I + c) =
+                make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+          } else {
+            *reinterpret_cast<uint2*>(out + m * p.ldo + c) =
+                make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+          }
+        }
+    }
+  }
+}
+
+template <int KIND, int BM, int BN, int MS, int WAVES_M>
+hipError_t launch_kind(const GemmArgs& a, int64_t grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((ggemm_kernel<KIND, BM, BN, MS, WAVES_M>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// Row-grouped kinds: pick the tile height from block_m (it must divide block_m).
+template <int KIND>
+hipError_t launch_rows(GemmArgs a, int64_t mcap, int n_per_tile, hipStream_t st) {
+  const int bm = a.block_m >= 128 ? 128 : a.block_m;
+  a.n_tiles_n = (int)((a.N + n_per_tile - 1) / n_per_tile);
+  const int64_t tiles = (mcap / bm) * a.n_tiles_n;
+  const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
+  switch (bm) {
+    case 128: return launch_kind<KIND, 128, 256, 32, 2>(a, grid, st);
+    case 64: return launch_kind<KIND, 64, 256, 32, 2>(a, grid, st);
+    case 32: return launch_kind<KIND, 32, 256, 32, 1>(a, grid, st);
+    case 16: return launch_kind<KIND, 16, 256, 16, 1>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
+                            const uint16_t* x_perm,
+                            const int32_t* tile_group, const int32_t* total_rows,
+                            const uint16_t* w1, const uint16_t* w2, uint16_t* h_save, uint16_t* a,
+                            uint16_t* y_perm, hipStream_t st) {
+  GemmArgs g{};
+  g.block_m = s.block_m;
+  g.I = s.I;
+  g.G = s.E + s.S;
+  g.tile_group = tile_group;
+  g.total_rows = total_rows;
+  // gate/up + SwiGLU: N counts gate columns (I); each tile covers BN/2 gate + BN/2 up columns.
+  g.a = x_perm; g.lda = s.H;
+  g.b = w1; g.ldb = s.H; g.b_gstride = (int64_t)2 * s.I * s.H;
+  g.out = a; g.ldo = s.I; g.out2 = h_save;
+  g.N = s.I; g.K = s.H;
+  if (which & MOE_FWD_GATEUP) {
+    hipError_t e = launch_rows<kFwdGateUp>(g, mcap, 128, st);
+    if (e != hipSuccess) return e;
+  }
+  if (!(which & MOE_FWD_DOWN)) return hipSuccess;
+  // down
+  g.a = a; g.lda = s.I;
+  g.b = w2; g.ldb = s.I; g.b_gstride = (int64_t)s.H * s.I;
+  g.out = y_perm; g.ldo = s.H; g.out2 = nullptr;
+  g.N = s.H; g.K = s.I;
+  return launch_rows<kFwdDown>(g, mcap, 256, st);
+}
+
+hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap,
+                              const uint16_t* dy_perm,
+                              const uint16_t* h_save, const int32_t* tile_group,
+                              const int32_t* total_rows, const uint16_t* w1, const uint16_t* w2,
+                              uint16_t* dh, uint16_t* dx_perm, hipStream_t st) {
+  GemmArgs g{};
+  g.block_m = s.block_m;
+  g.I = s.I;
+  g.G = s.E + s.S;
+  g.tile_group = tile_group;
+  g.total_rows = total_rows;
+  // da = dy_perm . W2[g] ([H, I] read as [K=H][N=I]) with the SwiGLU backward epilogue -> dh.
+  g.a = dy_perm; g.lda = s.H;
+  g.b = w2; g.ldb = s.I; g.b_gstride = (int64_t)s.H * s.I;
+  g.aux = h_save; g.out = dh;
+  g.N = s.I; g.K = s.H;
+  if (which & MOE_DGRAD_DOWN) {
+    hipError_t e = launch_rows<kDgradDown>(g, mcap, 256, st);
+    if (e != hipSuccess) return e;
+  }
+  if (!(which & MOE_DGRAD_GATEUP)) return hipSuccess;
+  // dx_perm = dh . W1[g] ([2I, H] read as [K=2I][N=H]).
+  g.a = dh; g.lda = 2 * (int64_t)s.I;
+  g.b = w1; g.ldb = s.H; g.b_gstride = (int64_t)2 * s.I * s.H;
+  g.aux = nullptr; g.out = dx_perm; g.ldo = s.H;
+  g.N = s.H; g.K = 2 * s.I;
+  return launch_rows<kDgradGateUp>(g, mcap, 256, st);
+}
+
+hipError_t launch_ggemm_wgrad(const moe_shape_t& s, uint32_t which, const uint16_t* x_perm,
+                              const uint16_t* a,
+                              const uint16_t* dy_perm, const uint16_t* dh,
+                              const int32_t* seg_offsets, uint16_t* dw1, uint16_t* dw2,
+                              hipStream_t st) {
+  GemmArgs g{};
+  g.I = s.I;
+  g.G = s.E + s.S;
+  g.seg = seg_offsets;
+  // dW2[g] [H, I] = dy_perm_seg^T . a_seg
+  g.a = dy_perm; g.lda = s.H;
+  g.b = a; g.ldb = s.I;
+  g.out = dw2; g.ldo = s.I; g.o_gstride = (int64_t)s.H * s.I;
+  g.M = s.H; g.N = s.I;
+  g.n_tiles_m = (g.M + 127) / 128;
+  g.n_tiles_n = (g.N + 255) / 256;
+  int64_t tiles = (int64_t)g.G * g.n_tiles_m * g.n_tiles_n;
+  if (which & MOE_WGRAD_DOWN) {
+    hipError_t e = launch_kind<kWgradDown, 128, 256, 32, 2>(
+        g, (tiles + kNumXcd - 1) / kNumXcd * kNumXcd, st);
+    if (e != hipSuccess) return e;
+  }
+  if (!(which & MOE_WGRAD_GATEUP)) return hipSuccess;
+  // dW1[g] [2I, H] = dh_seg^T . x_perm_seg
+  g.a = dh; g.lda = 2 * (int64_t)s.I;
+  g.b = x_perm; g.ldb = s.H;
+  g.out = dw1; g.ldo = s.H; g.o_gstride = (int64_t)2 * s.I * s.H;
+  g.M = 2 * s.I; g.N = s.H;
+  g.n_tiles_m = (g.M + 127) / 128;
+  g.n_tiles_n = (g.N + 255) / 256;
+  tiles = (int64_t)g.G * g.n_tiles_m * g.n_tiles_n;
+  return launch_kind<kWgradGateUp, 128, 256, 32, 2>(g, (tiles + kNumXcd - 1) / kNumXcd * kNumXcd,
+                                                    st);
+}
+
+}  // namespace moe

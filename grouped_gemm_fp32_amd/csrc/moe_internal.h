@@ -1,0 +1,55 @@
+// Internal launchers behind the C ABI (moe_api.hip validates arguments, then calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Token block used by the permutation's per-block histograms (a function of T only).
+int permute_token_block(int T);
+int64_t permute_num_blocks(int T);
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st);
+
+hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg,
+                        const float* logit_bias, const float* sel_bias, float* logits,
+                        float* probs, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                        hipStream_t st);
+
+hipError_t launch_permute(const moe_shape_t& s, int64_t mcap, const int32_t* topk_idx,
+                          const uint16_t* x, int32_t* seg_offsets, int32_t* tile_group,
+                          int32_t* total_rows, int32_t* row_token, int32_t* pos, uint16_t* x_perm,
+                          int32_t* ws, hipStream_t st);
+
+hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap, const uint16_t* x_perm,
+                            const int32_t* tile_group, const int32_t* total_rows,
+                            const uint16_t* w1, const uint16_t* w2, uint16_t* h_save, uint16_t* a,
+                            uint16_t* y_perm, hipStream_t st);
+
+hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap, const uint16_t* dy_perm,
+                              const uint16_t* h_save, const int32_t* tile_group,
+                              const int32_t* total_rows, const uint16_t* w1, const uint16_t* w2,
+                              uint16_t* dh, uint16_t* dx_perm, hipStream_t st);
+
+hipError_t launch_ggemm_wgrad(const moe_shape_t& s, uint32_t which, const uint16_t* x_perm, const uint16_t* a,
+                              const uint16_t* dy_perm, const uint16_t* dh,
+                              const int32_t* seg_offsets, uint16_t* dw1, uint16_t* dw2,
+                              hipStream_t st);
+
+hipError_t launch_combine(const moe_shape_t& s, const uint16_t* y_perm, const int32_t* pos,
+                          const float* topk_w, const int32_t* seg_offsets, uint16_t* y,
+                          hipStream_t st);
+
+hipError_t launch_combine_bwd(const moe_shape_t& s, int64_t mcap, const uint16_t* dy,
+                              const uint16_t* y_perm, const int32_t* pos, const float* topk_w,
+                              const int32_t* seg_offsets, const int32_t* row_token,
+                              const int32_t* total_rows, uint16_t* dy_perm, float* dtopk_w,
+                              hipStream_t st);
+
+hipError_t launch_unpermute_bwd(const moe_shape_t& s, const uint16_t* dx_perm, const int32_t* pos,
+                                const int32_t* seg_offsets, uint16_t* dx, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,135 @@
+"""C ABI checks that need no GPU: the library loads, exports every function include/moe.h declares,
+and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+
+import pytest
+
+import grouped_gemm_fp32_amd as M
+from oracle import moe_oracle as O
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.library_path()):
+        from grouped_gemm_fp32_amd import build
+        build.build()
+    return M.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = M.declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"libmoe.so does not export {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert M.moe_abi_version() >= 1
+    assert M.moe_status_string(0) == "MOE_OK"
+    assert M.moe_status_string(-1) == "MOE_ERR_INVALID_ARG"
+    assert M.moe_status_string(-3) == "MOE_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("T,E,K,S,B", [(64, 8, 2, 1, 16), (8192, 128, 6, 0, 128),
+                                       (16384, 128, 6, 2, 128), (256, 128, 6, 2, 16),
+                                       (0, 8, 2, 1, 16), (1, 4, 4, 4, 256), (1000, 256, 8, 3, 64)])
+def test_row_capacity_matches_oracle(lib, T, E, K, S, B):
+    s = M.make_shape(T, 256, E, K, 128, S, B)
+    assert M.moe_row_capacity(s) == O.row_capacity(T, E, K, S, B)
+
+
+def _call(lib, fn, *args):
+    return getattr(lib, fn)(*args)
+
+
+def test_shape_validation(lib):
+    bad = [
+        (M.make_shape(8, 256, 8, 9, 128, 0, 16), -1),     # K > E
+        (M.make_shape(8, 256, 8, 0, 128, 0, 16), -1),     # K < 1
+        (M.make_shape(-1, 256, 8, 2, 128, 0, 16), -1),    # T < 0
+        (M.make_shape(8, 256, 8, 2, 128, 0, 48), -2),     # block_m not supported
+        (M.make_shape(8, 200, 8, 2, 128, 0, 16), -2),     # H % 128
+        (M.make_shape(8, 256, 8, 2, 96, 0, 16), -2),      # I % 64
+        (M.make_shape(8, 256, 300, 2, 128, 0, 16), -2),   # E > 256
+        (M.make_shape(8, 256, 8, 2, 128, 0, 16, flags=0x80), -1),
+    ]
+    dummy = ctypes.c_void_p(16)
+    for s, code in bad:
+        st = lib.moe_route(ctypes.byref(s), None, dummy, None, None, dummy, None, dummy, dummy,
+                           None, None)
+        assert st == code, (s, st)
+        assert M.moe_row_capacity(s) == -1
+    assert lib.moe_row_capacity(None) == -1
+    assert lib.moe_route(None, *([None] * 10)) == -1
+
+
+def test_null_required_pointers(lib):
+    s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
+    d = ctypes.c_void_p(16)
+    # moe_route: topk outputs required; x given needs w_gate; x NULL needs logits
+    assert lib.moe_route(ctypes.byref(s), d, None, None, None, None, None, d, d, None, None) == -1
+    assert lib.moe_route(ctypes.byref(s), None, None, None, None, None, None, d, d, None, None) == -1
+    assert lib.moe_route(ctypes.byref(s), None, None, None, None, d, None, None, d, None, None) == -1
+    s_probs = M.make_shape(8, 256, 8, 2, 128, 1, 16, flags=M.MOE_PROBS_IN)
+    assert lib.moe_route(ctypes.byref(s_probs), None, None, None, None, None, None, d, d, None,
+                         None) == -1
+    # moe_permute
+    args = [d] * 8
+    for i in range(7):
+        a = list(args)
+        a[i] = None if i != 1 else d  # x (index 1) is optional
+        if i == 1:
+            continue
+        assert lib.moe_permute(ctypes.byref(s), *a, d, 1 << 20, None) == -1
+    # grouped_gemm_fwd: h_save (index 6) is optional, the rest required for both stages
+    for i in range(9):
+        if i == 6:
+            continue
+        a = [d] * 9
+        a[i] = None
+        assert lib.grouped_gemm_fwd(ctypes.byref(s), M.MOE_FWD, *a, None) == -1
+    assert lib.grouped_gemm_fwd(ctypes.byref(s), 0, *([d] * 9), None) == -1
+    assert lib.grouped_gemm_fwd(ctypes.byref(s), 4, *([d] * 9), None) == -1
+    # grouped_gemm_bwd: which must be DGRAD and/or WGRAD
+    assert lib.grouped_gemm_bwd(ctypes.byref(s), 0, *([d] * 13), None) == -1
+    assert lib.grouped_gemm_bwd(ctypes.byref(s), 16, *([d] * 13), None) == -1
+    a = [d] * 13
+    a[1] = None   # h_save needed by DGRAD
+    assert lib.grouped_gemm_bwd(ctypes.byref(s), M.MOE_DGRAD, *a, None) == -1
+    a = [d] * 13
+    a[11] = None  # dw1 needed by WGRAD
+    assert lib.grouped_gemm_bwd(ctypes.byref(s), M.MOE_WGRAD, *a, None) == -1
+    for fn, n in (("moe_combine", 5), ("moe_unpermute_bwd", 4), ("moe_combine_bwd", 9)):
+        for i in range(n):
+            a = [d] * n
+            a[i] = None
+            assert _call(lib, fn, ctypes.byref(s), *a, None) == -1, (fn, i)
+    assert "NULL" in M.moe_last_error()
+
+
+def test_workspace_too_small(lib):
+    s = M.make_shape(1000, 256, 8, 2, 128, 1, 16)
+    need = M.moe_workspace_size(s)
+    assert need == 4 * 4 * 8  # 4 token blocks of 256, 8 experts
+    d = ctypes.c_void_p(16)
+    assert lib.moe_permute(ctypes.byref(s), d, d, d, d, d, d, d, d, d, need - 1, None) == -3
+
+
+def test_empty_batch_is_a_noop_on_the_host(lib):
+    s = M.make_shape(0, 256, 8, 2, 128, 1, 16)
+    d = ctypes.c_void_p(16)
+    assert lib.moe_route(ctypes.byref(s), d, d, None, None, None, None, d, d, None, None) == 0
+    assert lib.grouped_gemm_fwd(ctypes.byref(s), M.MOE_FWD, *([d] * 9), None) == 0
+    assert lib.moe_combine(ctypes.byref(s), *([d] * 5), None) == 0
+    assert lib.moe_unpermute_bwd(ctypes.byref(s), *([d] * 4), None) == 0
+    assert lib.grouped_gemm_bwd(ctypes.byref(s), M.MOE_DGRAD, *([d] * 13), None) == 0
+
+
+def test_binding_refuses_host_tensors(lib):
+    import torch
+    s = M.make_shape(4, 256, 8, 2, 128, 0, 16)
+    t = torch.zeros(4, 2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        M.moe_route(s, None, None, None, None, torch.zeros(4, 8), None, t, torch.zeros(4, 2), None,
+                    stream=0)
