@@ -89,6 +89,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before warmup, copy a cold buffer of this many MiB (a plain copy of known "
+                         "size that scales the HBM byte counters)")
     ap.add_argument("--cpu-sample", type=int, default=1024,
                     help="tokens of the workload the CPU oracle runs (0 = skip the CPU baseline)")
     args = ap.parse_args()
@@ -154,6 +157,16 @@ def main():
         M.moe_unpermute_bwd(s, b["dx_perm"], b["pos"], b["seg_offsets"], b["dx"])
         mark(11)
 
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.int32, device=dev)
+        flush = torch.ones(2 * n, dtype=torch.int32, device=dev)   # evicts src from the caches
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + written")
+        del src, flush, dst
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()

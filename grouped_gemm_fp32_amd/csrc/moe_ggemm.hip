@@ -131,6 +131,9 @@ template <int ROWS> struct LoaderK {
 
 // Row-contiguous source ([K][rows] in HBM): element (r, k) at base + k*ld + r. Each thread takes
 // 8x8 blocks: 8 loads of 8 rows at consecutive k, transposed in registers, 8 LDS row writes.
+// Lanes run over the 8 k-blocks of a row block first: a load instruction then reads 128
+// contiguous bytes per k row, and the 8 lanes of a row block write one contiguous 128-byte LDS
+// span (a row-block-major order would put lanes 1152 bytes apart: 16-way bank conflicts).
 template <int ROWS> struct LoaderT {
   static constexpr int kBlocks = (ROWS / 8) * (kBK / 8);
   static constexpr int kIters = (kBlocks + kThreads - 1) / kThreads;
@@ -140,7 +143,7 @@ template <int ROWS> struct LoaderT {
 #pragma unroll
     for (int i = 0; i < kIters; ++i) {
       const int b = tid + i * kThreads;
-      const int rb = b % (ROWS / 8), kb = b / (ROWS / 8);
+      const int kb = b & 7, rb = b >> 3;  // 8 lanes cover one row block's 8 k-blocks
       const bool ok = (kBlocks % kThreads == 0 || b < kBlocks) && rb * 8 < rlim;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -155,7 +158,7 @@ template <int ROWS> struct LoaderT {
     for (int i = 0; i < kIters; ++i) {
       const int b = tid + i * kThreads;
       if (kBlocks % kThreads == 0 || b < kBlocks) {
-        const int rb = b % (ROWS / 8), kb = b / (ROWS / 8);
+        const int kb = b & 7, rb = b >> 3;
         uint4 t[8];
         transpose8x8(v[i], t);
 #pragma unroll
