@@ -173,7 +173,7 @@ moe_status_t grouped_gemm_fwd(const moe_shape_t* s, uint32_t which, const uint16
     REQUIRE(w2);
     REQUIRE(y_perm);
   }
-  return hip_status(moe::launch_ggemm_fwd(*s, which, capacity(s), x_perm, tile_group, total_rows,
+  return hip_status(moe::launch_ggemm_fwd(*s, which, capacity(s), x_perm, seg_offsets, tile_group, total_rows,
                                           w1, w2, h_save, a, y_perm, (hipStream_t)stream),
                     "grouped_gemm_fwd");
 }
@@ -191,6 +191,7 @@ moe_status_t grouped_gemm_bwd(const moe_shape_t* s, uint32_t which, const uint16
   }
   const bool rows = s->T > 0;  // with T == 0 no activation row is read and dgrad is a no-op
   if (rows && (which & MOE_DGRAD)) {
+    REQUIRE(seg_offsets);
     REQUIRE(tile_group);
     REQUIRE(total_rows);
     REQUIRE(dh);
@@ -222,7 +223,7 @@ moe_status_t grouped_gemm_bwd(const moe_shape_t* s, uint32_t which, const uint16
   hipStream_t st = (hipStream_t)stream;
   if (rows && (which & MOE_DGRAD)) {
     moe_status_t r = hip_status(moe::launch_ggemm_dgrad(*s, which, capacity(s), dy_perm, h_save,
-                                                        tile_group, total_rows, w1, w2, dh,
+                                                        seg_offsets, tile_group, total_rows, w1, w2, dh,
                                                         dx_perm, st),
                                 "grouped_gemm_bwd(dgrad)");
     if (r != MOE_OK) return r;

@@ -25,12 +25,14 @@ hipError_t launch_permute(const moe_shape_t& s, int64_t mcap, const int32_t* top
                           int32_t* ws, hipStream_t st);
 
 hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap, const uint16_t* x_perm,
-                            const int32_t* tile_group, const int32_t* total_rows,
+                            const int32_t* seg_offsets, const int32_t* tile_group,
+                            const int32_t* total_rows,
                             const uint16_t* w1, const uint16_t* w2, uint16_t* h_save, uint16_t* a,
                             uint16_t* y_perm, hipStream_t st);
 
 hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap, const uint16_t* dy_perm,
-                              const uint16_t* h_save, const int32_t* tile_group,
+                              const uint16_t* h_save, const int32_t* seg_offsets,
+                              const int32_t* tile_group,
                               const int32_t* total_rows, const uint16_t* w1, const uint16_t* w2,
                               uint16_t* dh, uint16_t* dx_perm, hipStream_t st);
 

@@ -209,18 +209,18 @@ def _compare_layer(buf, f, b):
     assert int(_np(buf["total_rows"])[0]) == total
     pad = f["row_token"][:total] < 0
     for name, ref in (("h_save", f["h"]), ("a", f["a"]), ("y_perm", f["y_perm"])):
-        got = vals_host(buf[name])[:total]
+        got = vals_host(buf[name][:total])
         assert np.all(got[pad] == 0), f"{name}: padding rows not zero"
         assert_bf16_close(got, ref, name)
     assert_bf16_close(vals_host(buf["y"]), f["y"], "y")
     if b is None:
         return
-    got = vals_host(buf["dy_perm"])[:total]
+    got = vals_host(buf["dy_perm"][:total])
     assert np.all(got[pad] == 0)
     assert_bf16_close(got, b["dy_perm"], "dy_perm")
     assert_bf16_close(_np(buf["dtopk_w"]), b["dtopk_w"], "dtopk_w", row_axis=0)
-    assert_bf16_close(vals_host(buf["dh"])[:total], b["dh"], "dh")
-    assert_bf16_close(vals_host(buf["dx_perm"])[:total], b["dx_perm"], "dx_perm")
+    assert_bf16_close(vals_host(buf["dh"][:total]), b["dh"], "dh")
+    assert_bf16_close(vals_host(buf["dx_perm"][:total]), b["dx_perm"], "dx_perm")
     assert_bf16_close(vals_host(buf["dw1"]), b["dw1"], "dw1")
     assert_bf16_close(vals_host(buf["dw2"]), b["dw2"], "dw2")
     assert_bf16_close(vals_host(buf["dx"]), b["dx"], "dx")
