@@ -92,7 +92,7 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, copy a cold buffer of this many MiB (a plain copy of known "
                          "size that scales the HBM byte counters)")
-    ap.add_argument("--cpu-sample", type=int, default=1024,
+    ap.add_argument("--cpu-sample", type=int, default=384,
                     help="tokens of the workload the CPU oracle runs (0 = skip the CPU baseline)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -163,7 +163,7 @@ def main():
         flush = torch.ones(2 * n, dtype=torch.int32, device=dev)   # evicts src from the caches
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.add(src, 1, out=dst)   # an ordinary elementwise kernel: reads and writes N MiB
         torch.cuda.synchronize()
         log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + written")
         del src, flush, dst

@@ -1,0 +1,134 @@
+"""Summaries of rocprofv3 CSV output for this library's kernels.
+
+    python -m grouped_gemm_fp32_amd.profiling stats <kernel_stats.csv>
+    python -m grouped_gemm_fp32_amd.profiling traffic <fetch_dir> <write_dir> --calib-mib N \
+        [--workload NAME] [--json OUT]
+
+`stats` prints the per-kernel table (calls, average and total duration, share of GPU time).
+`traffic` reads two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (KiB per dispatch) of
+the same deterministic program, scales each counter by what it reads for a plain copy of a known
+size in the same run (the dispatch with the largest FETCH_SIZE outside this library: bench.py's
+`--calib-copy-mib` elementwise copy of a cold buffer, `calib` MiB read and written; the same
+dispatch id in the WRITE_SIZE run), and reports HBM bytes per launch.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import json
+import os
+import re
+import sys
+
+# rocprofv3 kernel name -> the stage names bench.py reports
+STAGE_OF = {
+    "ggemm_tall_kernel<0>": "fwd_gateup", "ggemm_tall_kernel<1>": "fwd_down",
+    "ggemm_tall_kernel<2>": "dgrad_down", "ggemm_tall_kernel<3>": "dgrad_gateup",
+    "ggemm_wgrad_kernel<4>": "wgrad_down", "ggemm_wgrad_kernel<5>": "wgrad_gateup",
+}
+
+
+def short_name(n: str) -> str:
+    m = re.search(r"moe::\(anonymous namespace\)::(\w+)(<[^(]*>)?", n)
+    if m:
+        return m.group(1) + (m.group(2) or "").replace(" ", "")
+    return n.split("(")[0][:60]
+
+
+def _csv(path_or_dir: str, suffix: str) -> str:
+    if os.path.isdir(path_or_dir):
+        hits = glob.glob(os.path.join(path_or_dir, "**", "*" + suffix), recursive=True)
+        if not hits:
+            raise FileNotFoundError(f"no *{suffix} under {path_or_dir}")
+        return hits[0]
+    return path_or_dir
+
+
+def stats_table(path: str) -> str:
+    rows = list(csv.DictReader(open(_csv(path, "kernel_stats.csv"))))
+    out = ["| kernel | stage | calls | avg (us) | total (ms) | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        k = short_name(r["Name"])
+        out.append(f"| {k} | {STAGE_OF.get(k, '')} | {r['Calls']} | "
+                   f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    return "\n".join(out)
+
+
+def counter_rows(path: str) -> list:
+    return list(csv.DictReader(open(_csv(path, "counter_collection.csv"))))
+
+
+def counter_means(path: str) -> dict:
+    d = collections.defaultdict(list)
+    for r in counter_rows(path):
+        d[(short_name(r["Kernel_Name"]), r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in d.items()}
+
+
+def traffic(fetch_dir: str, write_dir: str, calib_mib: float) -> dict:
+    known = calib_mib * 2 ** 20
+    fr, wr = counter_rows(fetch_dir), counter_rows(write_dir)
+    foreign = [r for r in fr if "moe::" not in r["Kernel_Name"]]
+    cal = max(foreign, key=lambda r: float(r["Counter_Value"]))
+    cal_w = [r for r in wr if r["Dispatch_Id"] == cal["Dispatch_Id"]]
+    if not cal_w or cal_w[0]["Kernel_Name"] != cal["Kernel_Name"]:
+        raise ValueError("the FETCH_SIZE and WRITE_SIZE runs do not line up by dispatch id")
+    out = {}
+    for name, rows, crow, counter in (("fetch", fr, cal, "FETCH_SIZE"),
+                                      ("write", wr, cal_w[0], "WRITE_SIZE")):
+        measured = float(crow["Counter_Value"]) * 1024.0
+        scale = known / measured
+        out[f"{name}_calibration"] = {"kernel": short_name(crow["Kernel_Name"]),
+                                      "dispatch": int(crow["Dispatch_Id"]), "known_bytes": known,
+                                      "counter_bytes": measured, "scale": scale}
+        d = collections.defaultdict(list)
+        for r in rows:
+            if r["Counter_Name"] == counter:
+                d[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        for k, v in d.items():
+            e = out.setdefault("kernels", {}).setdefault(k, {})
+            e[f"{name}_bytes"] = sum(v) / len(v) * 1024.0 * scale
+            e[f"{name}_bytes_raw"] = sum(v) / len(v) * 1024.0
+    for k, e in out.get("kernels", {}).items():
+        e["bytes_per_launch"] = e.get("fetch_bytes", 0.0) + e.get("write_bytes", 0.0)
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch")
+    t.add_argument("write")
+    t.add_argument("--calib-mib", type=float, required=True)
+    t.add_argument("--workload", default="c2")
+    t.add_argument("--json", default=None, help="merge per-stage bytes into this traffic.json")
+    t.add_argument("--source-hash", default=None)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print(stats_table(a.csv))
+        return
+    tr = traffic(a.fetch, a.write, a.calib_mib)
+    print(json.dumps(tr, indent=1))
+    if a.json:
+        d = json.load(open(a.json)) if os.path.exists(a.json) else {}
+        for k, e in tr["kernels"].items():
+            if k in STAGE_OF:
+                d[f"{a.workload}:{STAGE_OF[k]}"] = {
+                    "bytes_per_launch": round(e["bytes_per_launch"]),
+                    "fetch_bytes": round(e.get("fetch_bytes", 0)),
+                    "write_bytes": round(e.get("write_bytes", 0)),
+                    "fetch_scale": tr["fetch_calibration"]["scale"],
+                    "write_scale": tr["write_calibration"]["scale"],
+                    "source_hash": a.source_hash}
+        with open(a.json, "w") as f:
+            json.dump(d, f, indent=1, sort_keys=True)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
