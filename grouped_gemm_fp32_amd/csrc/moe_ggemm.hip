@@ -18,6 +18,8 @@
 //   DgradGateUp dx_perm = dh . W1[g]
 //   WgradDown   dW2[g] = dy_perm_seg^T . a_seg        (contraction over the segment's rows)
 //   WgradGateUp dW1[g] = dh_seg^T . x_perm_seg
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -373,31 +375,36 @@ __global__ __launch_bounds__(kThreads, 2) void ggemm_kernel(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// DMA engine (tiles of 64 to 256 rows). Taller tiles load fewer bytes per FLOP, and a segment is a
-// whole number of 128-row blocks of one expert, so a tile may take two consecutive blocks
-// (256 rows) and still belong to a single expert. Each workgroup derives its tile from
-// seg_offsets: group g has ceil(len_g / 256) tiles of 256 rows, the last one 128 or 256.
-// (Measured on MI355X at 8192 tokens x 128 experts: 384-row tiles, which only fit two LDS
-// stages and 384 accumulators, ran 1.7x slower than 256-row tiles.)
-// Weight-gradient tiles are 256 weight rows.
+// DMA engine (tiles of 64 to 384 rows). A segment is a whole number of block_m-row blocks of one
+// expert, so a tile may span several consecutive 128-row blocks and still belong to one expert.
+// The tall kernel cuts every segment into ceil(len / 384) tiles of 128, 256 or 384 rows, as even
+// as the 128-row granularity allows; an expert with 384 rows then streams each weight panel once,
+// where 128- or 256-row tiles would stream it two or three times.
 //
-// Every operand goes from HBM to LDS through the bounds-checked buffer->LDS DMA
-// (buffer_load_dwordx4 ... lds): lane l of a wavefront deposits its 16 bytes at LDS base + 16 l,
+// Operands go from HBM to LDS through the bounds-checked buffer->LDS DMA
+// (buffer_load_dwordx4 ... lds): lane l of a wavefront deposits its 16 bytes at LDS M0 + 16 l,
 // whatever address it loaded, and reads past the buffer resource's size return zero (tile tails
-// and segment ends need no special code). A ring of two or three LDS stages, one barrier per
-// k-step.
-//   K-major operand (K contiguous in HBM): LDS [rows][64], 16-byte chunk c of row r stored at
-//     position c ^ (r & 7) so the MFMA fragment reads (32 rows, one chunk) hit 8 distinct bank
-//     groups.
-//   MN-major operand (rows contiguous in HBM, [k][rows]): LDS [64][rows] as in HBM, chunk cc of
-//     k-row k stored at cc ^ ((k & 3) << 2); fragments come from ds_read_tr16_b64, which hands
+// and segment ends need no special code). A ring of up to four stages of BK k.
+//   K-major operand (K contiguous in HBM): LDS [rows][BK]; 16-byte chunk c of row r sits at
+//     position c ^ swz(r) (swz = r & 7 with 8 chunks per row, (r >> 1) & 3 with 4), so the 32
+//     rows of a fragment read spread over all banks.
+//   MN-major operand (rows contiguous in HBM, [k][rows]): LDS [BK][rows] as in HBM, chunk cc of
+//     k-row k stored at cc ^ ((k & 3) << 2); fragments come from ds_read_b64_tr_b16, which hands
 //     each lane 4 consecutive k of one column (within 16 lanes: lane i, item q <- lane 4q + i/4,
 //     item i % 4), two reads per 32x32x16 operand.
-// Four wavefronts in 2 x 2, each (BM/2) x 128 of the BM x 256 tile.
+// Four wavefronts, WM x WN, each (BM/WM) x (BN/WN) of the tile, v_mfma_f32_32x32x16_bf16 with the
+// B fragment as the first operand so that a lane ends with 4 consecutive output columns.
+//
+// Pipeline: the fragments of the next 16-k slice are read from LDS while the MFMAs of the current
+// slice run. The one barrier per stage sits before the stage's last slice: every wave then holds
+// that slice's fragments in registers, so the barrier both publishes the next stage (whose DMA
+// each wave has waited for) and frees the current stage's slot, which is refilled at once with
+// the stage STAGES ahead. STAGES - 1 stages are in flight while a stage is computed.
 // ------------------------------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u32_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
 // Buffer resource (gfx9 layout): 48-bit base, stride 0, num_records = bytes, raw dword format.
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -412,276 +419,94 @@ __device__ __forceinline__ v4u32_t make_rsrc(const void* base, int64_t bytes) {
   return r;
 }
 
-// Bounds-checked DMA of 16 bytes per lane from a buffer resource into LDS at lds_wave + 16 * lane. Issued from asm: the instruction has no register result (it
-// writes LDS through M0), and hiding it from the compiler keeps it from draining every DMA
-// before unrelated LDS reads; the kernel's own vmcnt waits and barriers order the data.
+// Bounds-checked DMA of 16 bytes per lane from a buffer resource into LDS at lds_wave + 16 * lane.
+// Issued from asm: the instruction has no register result (it writes LDS through M0), and hiding
+// it from the compiler keeps it from draining every DMA before unrelated LDS reads; the kernel's
+// own vmcnt waits and barriers order the data.
 __device__ __forceinline__ void dma16(v4u32_t r, uint32_t voff, uint32_t lds_wave) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(uniform(lds_wave)), "v"(voff), "s"(r) : "memory", "m0");
 }
 
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+// Waits, each also a compiler memory barrier so that no LDS access moves across them.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// s_waitcnt lgkmcnt(0) (LDS reads retired), vmcnt and expcnt left at their maxima.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
-
-typedef uint32_t v2u32_t __attribute__((ext_vector_type(2)));
-
-// N transposed 8-byte LDS reads (ds_read_b64_tr_b16) in one asm block that also waits for them,
-// so the results are complete when the block ends. addr: LDS byte addresses.
-template <int N>
-__device__ __forceinline__ void tr_read(v2u32_t (&v)[N], const uint32_t (&addr)[N]);
-
-template <>
-__device__ __forceinline__ void tr_read<8>(v2u32_t (&v)[8], const uint32_t (&a)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-        "=&v"(v[6]), "=&v"(v[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-}
-
-template <>
-__device__ __forceinline__ void tr_read<12>(v2u32_t (&v)[12], const uint32_t (&a)[12]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %12\n\tds_read_b64_tr_b16 %1, %13\n\t"
-      "ds_read_b64_tr_b16 %2, %14\n\tds_read_b64_tr_b16 %3, %15\n\t"
-      "ds_read_b64_tr_b16 %4, %16\n\tds_read_b64_tr_b16 %5, %17\n\t"
-      "ds_read_b64_tr_b16 %6, %18\n\tds_read_b64_tr_b16 %7, %19\n\t"
-      "ds_read_b64_tr_b16 %8, %20\n\tds_read_b64_tr_b16 %9, %21\n\t"
-      "ds_read_b64_tr_b16 %10, %22\n\tds_read_b64_tr_b16 %11, %23\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-        "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-        "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11])
-      : "memory");
-}
-
-template <>
-__device__ __forceinline__ void tr_read<4>(v2u32_t (&v)[4], const uint32_t (&a)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\tds_read_b64_tr_b16 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-      : "memory");
+// Wait until at most `later` of this wave's DMA stages (PER instructions each) are in flight.
+template <int PER, int MAXL>
+__device__ __forceinline__ void wait_stages(int later) {
+  if constexpr (MAXL >= 3) {
+    if (later >= 3) { wait_vm<3 * PER>(); return; }
+  }
+  if constexpr (MAXL >= 2) {
+    if (later == 2) { wait_vm<2 * PER>(); return; }
+  }
+  if constexpr (MAXL >= 1) {
+    if (later == 1) { wait_vm<PER>(); return; }
+  }
+  wait_vm<0>();
 }
 
 constexpr int kLdsBytes = 163840;   // gfx950: 160 KiB of LDS per workgroup
-constexpr int kTallRows = 256;      // tallest row-grouped tile (two 128-row blocks)
+constexpr int kTallBlk = 128;       // row granularity of tall tiles (block_m % 128 == 0)
+constexpr int kTallMaxBlk = 3;      // tallest tile: 3 blocks = 384 rows
 
-template <int BM> struct DmaCfg {
-  static constexpr int BN = 256, WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
-  static constexpr int A_BYTES = BM * kBK * 2, B_BYTES = BN * kBK * 2;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int STAGES = 3 * STAGE <= kLdsBytes ? 3 : 2;
+template <int BM_, int BN_, int WM_, int BK_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 4 / WM_, BK = BK_;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32, KK = BK / 16;
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
+  static constexpr int STAGES = kLdsBytes / STAGE >= 4 ? 4 : kLdsBytes / STAGE;
   static constexpr int LA = A_BYTES / 4096, LB = B_BYTES / 4096;  // DMA instr per lane per stage
-  static_assert(2 * STAGE <= kLdsBytes, "two stages must fit in LDS");
+  static_assert(WM * WN == 4 && TM * 32 == WTM && TN * 32 == WTN, "wave tiling");
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "whole DMA rounds");
+  static_assert(STAGES >= 2, "two stages must fit in LDS");
+  static_assert((STAGES - 1) * (LA + LB) < 64, "vmcnt range");
 };
 
-// One BM x 256 output tile: rows m0.. of group g (row-grouped kinds) or weight rows m0.. of group
-// g (wgrad), contraction over [kbeg, kbeg + klen).
-template <int KIND, int BM>
-__device__ __forceinline__ void dma_tile(const GemmArgs& p, unsigned char* smem, uint32_t lds_base,
-                                         int g, int m0, int n0, int kbeg, int klen) {
+// K-major LDS position of 16-byte chunk c of row r (an involution, so it also maps back).
+template <int BK>
+__device__ __forceinline__ int kswz(int r, int c) {
+  if constexpr (BK == 64) return c ^ (r & 7);
+  else return c ^ ((r >> 1) & 3);
+}
+
+// Epilogue shared by the engines: lane -> row, registers -> 4 consecutive columns per group.
+template <int KIND, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16_t (&acc)[TM][TN], int g,
+                                           int m0, int n0, int wm, int wn, int lane) {
   typedef KindTraits<KIND> Tr;
   typedef Mfma<32> Mf;
-  typedef DmaCfg<BM> C;
-  constexpr int BN = C::BN, WTM = C::WTM, WTN = C::WTN, TM = C::TM, TN = C::TN;
-  constexpr int A_BYTES = C::A_BYTES, STAGE = C::STAGE, STAGES = C::STAGES;
-  constexpr int LA = C::LA, LB = C::LB;
-  constexpr bool AMN = Tr::a_trans, BMN = Tr::b_trans;
-  static_assert(!Tr::split || TN == 4, "split needs 2 gate + 2 up sub-tiles");
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // ---- buffer resources: each covers exactly the bytes this tile may read ----------------------
-  v4u32_t ra, rb;
-  if (AMN) ra = make_rsrc(p.a + (int64_t)kbeg * p.lda, (int64_t)klen * p.lda * 2);
-  else ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)BM * p.lda * 2);
-  const uint16_t* b_grp = p.b + (int64_t)g * p.b_gstride;
-  if (Tr::grouped_rows) rb = make_rsrc(b_grp, p.b_gstride * 2);
-  else rb = make_rsrc(p.b + (int64_t)kbeg * p.ldb, (int64_t)klen * p.ldb * 2);
-
-  // ---- per-lane DMA byte offsets of stage 0 (a k-step adds a fixed stride) ---------------------
-  // K-major: instruction i of wave w fills rows (i*4 + w)*8 .. +8; lane -> row + chunk position.
-  // MN-major: instruction i of wave w fills flat chunks (i*4 + w)*64 + lane of [64][ROWS].
-  uint32_t a_off[LA], b_off[LB];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    if (!AMN) {
-      const int r = (i * 4 + wave) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (r & 7);
-      a_off[i] = (uint32_t)(((int64_t)r * p.lda + c * 8) * 2);
-    } else {
-      constexpr int CPR = BM / 8;
-      const int f = (i * 4 + wave) * 64 + lane;
-      const int k = f / CPR, cc = (f % CPR) ^ ((k & 3) << 2);
-      a_off[i] = (uint32_t)(((int64_t)k * p.lda + m0 + cc * 8) * 2);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    if (!BMN) {
-      const int r = (i * 4 + wave) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (r & 7);
-      int64_t row;
-      if (Tr::split) row = r < BN / 2 ? n0 + r : p.I + n0 + (r - BN / 2);
-      else row = n0 + r;
-      b_off[i] = (uint32_t)((row * p.ldb + c * 8) * 2);
-    } else {
-      constexpr int CPR = BN / 8;
-      const int f = (i * 4 + wave) * 64 + lane;
-      const int k = f / CPR, cc = (f % CPR) ^ ((k & 3) << 2);
-      b_off[i] = (uint32_t)(((int64_t)k * p.ldb + n0 + cc * 8) * 2);
-    }
-  }
-  const uint32_t a_kstep = AMN ? (uint32_t)(kBK * p.lda * 2) : (uint32_t)(kBK * 2);
-  const uint32_t b_kstep = BMN ? (uint32_t)(kBK * p.ldb * 2) : (uint32_t)(kBK * 2);
-
-  auto issue = [&](int kt, int slot) {
-    const uint32_t sa = lds_base + slot * STAGE;
-    const uint32_t sb = sa + A_BYTES;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) dma16(ra, a_off[i] + kt * a_kstep, sa + (i * 4 + wave) * 1024);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) dma16(rb, b_off[i] + kt * b_kstep, sb + (i * 4 + wave) * 1024);
-  };
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-  // LDS row (K-major) or column (MN-major) of the wave's sub-tile j.
-  auto b_row = [&](int j) {
-    if (Tr::split) return (j >> 1) * (BN / 2) + wn * (WTN / 2) + (j & 1) * 32;
-    return wn * WTN + j * 32;
-  };
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int grp = lane >> 4, li = lane & 15;
-  auto frag_k = [&](const unsigned char* base, int row0, int kk) -> bf16x8_t {
-    const int r = row0 + l32;
-    const int c = (2 * kk + hi) ^ (r & 7);
-    return *reinterpret_cast<const bf16x8_t*>(base + r * 128 + c * 16);
-  };
-  // MN-major fragment addresses: two transposed 8-byte reads give columns col0 + (grp&1)*16 + li,
-  // k = kk*16 + (grp>>1)*8 + 0..7.
-  auto tr_addr = [&](int rows, int col0, int kk, int h) -> uint32_t {
-    const int col = col0 + (grp & 1) * 16 + 4 * (li & 3);
-    const int k = kk * 16 + (grp >> 1) * 8 + (li >> 2) + 4 * h;
-    const int cc = (col >> 3) ^ ((k & 3) << 2);
-    return (uint32_t)(k * rows * 2 + cc * 16 + ((col >> 2) & 1) * 8);
-  };
-
-  const int nk = (klen + kBK - 1) / kBK;
-  constexpr int AHEAD = STAGES - 1;   // stages in flight ahead of the one computed
-#pragma unroll
-  for (int s0 = 0; s0 < AHEAD; ++s0)
-    if (s0 < nk) issue(s0, s0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // This wave's DMA for stage kt is done once only the stages issued after it remain; the
-    // barrier then publishes every wave's stage kt and retires every wave's reads of stage
-    // kt - 1, whose slot the next DMA reuses. A bare s_barrier: __syncthreads() would add a
-    // fence that also drains the DMA still in flight.
-    const int later = min(AHEAD - 1, nk - 1 - kt);   // stages issued after kt
-    if (later >= 2) wait_vm<2 * (LA + LB)>();
-    else if (later == 1) wait_vm<LA + LB>();
-    else wait_vm<0>();
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    if (kt + AHEAD < nk) issue(kt + AHEAD, (kt + AHEAD) % STAGES);
-    const unsigned char* sa = smem + (kt % STAGES) * STAGE;
-    const unsigned char* sb = sa + A_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8_t af[TM], bf[TN];
-      // Transposed reads are issued from inline asm blocks that wait for them: the builtin form
-      // makes the compiler drain every outstanding DMA first.
-      if constexpr (AMN) {
-        static_assert(TM % 4 == 0, "transposed A in groups of four sub-tiles");
-#pragma unroll
-        for (int i0 = 0; i0 < TM; i0 += 4) {
-          uint32_t ad[8];
-          v2u32_t v[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t base = lds_base + (uint32_t)(sa - smem);
-            ad[2 * i] = base + tr_addr(BM, wm * WTM + (i0 + i) * 32, kk, 0);
-            ad[2 * i + 1] = base + tr_addr(BM, wm * WTM + (i0 + i) * 32, kk, 1);
-          }
-          tr_read<8>(v, ad);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) __builtin_memcpy(&af[i0 + i], &v[2 * i], 16);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = frag_k(sa, wm * WTM + i * 32, kk);
-      }
-      if constexpr (BMN) {
-        uint32_t ad[8];
-        v2u32_t v[8];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const uint32_t base = lds_base + (uint32_t)(sb - smem);
-          ad[2 * j] = base + tr_addr(BN, b_row(j), kk, 0);
-          ad[2 * j + 1] = base + tr_addr(BN, b_row(j), kk, 1);
-        }
-        tr_read<8>(v, ad);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) __builtin_memcpy(&bf[j], &v[2 * j], 16);
-      } else {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = frag_k(sb, b_row(j), kk);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = Mf::run(bf[j], af[i], acc[i][j]);
-    }
-  }
-
-  // ---- epilogue (lane -> row, registers -> 4 consecutive columns per group) --------------------
   const int m_in = Mf::out_m(lane);
   if constexpr (Tr::split) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int64_t m = m0 + wm * WTM + i * 32 + m_in;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < TN / 2; ++jj)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = n0 + wn * (WTN / 2) + jj * 32 + Mf::out_n(lane, q);
           if (c >= p.I) continue;
+          const f32x16_t& ga = acc[i][jj];
+          const f32x16_t& ua = acc[i][jj + TN / 2];
           float av[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) av[e] = silu_f(acc[i][jj][4 * q + e]) * acc[i][jj + 2][4 * q + e];
+          for (int e = 0; e < 4; ++e) av[e] = silu_f(ga[4 * q + e]) * ua[4 * q + e];
           *reinterpret_cast<uint2*>(p.out + m * p.ldo + c) =
               make_uint2(pack_bf2(av[0], av[1]), pack_bf2(av[2], av[3]));
           if (p.out2) {
             uint16_t* hrow = p.out2 + m * (2 * (int64_t)p.I);
             *reinterpret_cast<uint2*>(hrow + c) =
-                make_uint2(pack_bf2(acc[i][jj][4 * q], acc[i][jj][4 * q + 1]),
-                           pack_bf2(acc[i][jj][4 * q + 2], acc[i][jj][4 * q + 3]));
+                make_uint2(pack_bf2(ga[4 * q], ga[4 * q + 1]), pack_bf2(ga[4 * q + 2], ga[4 * q + 3]));
             *reinterpret_cast<uint2*>(hrow + p.I + c) =
-                make_uint2(pack_bf2(acc[i][jj + 2][4 * q], acc[i][jj + 2][4 * q + 1]),
-                           pack_bf2(acc[i][jj + 2][4 * q + 2], acc[i][jj + 2][4 * q + 3]));
+                make_uint2(pack_bf2(ua[4 * q], ua[4 * q + 1]), pack_bf2(ua[4 * q + 2], ua[4 * q + 3]));
           }
         }
     }
@@ -726,13 +551,394 @@ __device__ __forceinline__ void dma_tile(const GemmArgs& p, unsigned char* smem,
   }
 }
 
-__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+// One tile: rows m0.. of group g (row-grouped kinds) or weight rows m0.. of group g (wgrad),
+// columns n0.., contraction over [kbeg, kbeg + klen).
+template <int KIND, class TL>
+__device__ __forceinline__ void pipe_tile(const GemmArgs& p, unsigned char* smem, int g, int m0,
+                                          int n0, int kbeg, int klen) {
+  typedef KindTraits<KIND> Tr;
+  typedef Mfma<32> Mf;
+  constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, WTM = TL::WTM, WTN = TL::WTN;
+  constexpr int TM = TL::TM, TN = TL::TN, KK = TL::KK;
+  constexpr int A_BYTES = TL::A_BYTES, STAGE = TL::STAGE, STAGES = TL::STAGES;
+  constexpr int LA = TL::LA, LB = TL::LB;
+  constexpr bool AMN = Tr::a_trans, BMN = Tr::b_trans;
+  static_assert(!Tr::split || TN % 2 == 0, "split needs gate and up sub-tiles in pairs");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
+  lds_u8_t* s3 = (lds_u8_t*)smem;
+
+  // ---- buffer resources: each covers exactly the bytes this tile may read ----------------------
+  v4u32_t ra, rb;
+  if (AMN) ra = make_rsrc(p.a + (int64_t)kbeg * p.lda, (int64_t)klen * p.lda * 2);
+  else ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)BM * p.lda * 2);
+  if (Tr::grouped_rows) rb = make_rsrc(p.b + (int64_t)g * p.b_gstride, p.b_gstride * 2);
+  else rb = make_rsrc(p.b + (int64_t)kbeg * p.ldb, (int64_t)klen * p.ldb * 2);
+
+  // ---- per-lane DMA byte offsets of stage 0 (a k-step adds a fixed stride) ---------------------
+  // K-major: instruction i of wave w fills rows (i*4 + w)*RPI .. +RPI, lane -> (row, position).
+  // MN-major: instruction i of wave w fills flat chunks (i*4 + w)*64 + lane of [BK][ROWS].
+  constexpr int CPR = BK / 8, RPI = 64 / CPR;
+  uint32_t a_off[LA], b_off[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    if constexpr (!AMN) {
+      const int r = (i * 4 + wave) * RPI + lane / CPR;
+      const int c = kswz<BK>(r, lane % CPR);
+      a_off[i] = (uint32_t)(((int64_t)r * p.lda + c * 8) * 2);
+    } else {
+      constexpr int CPRM = BM / 8;
+      const int f = (i * 4 + wave) * 64 + lane;
+      const int k = f / CPRM, cc = (f % CPRM) ^ ((k & 3) << 2);
+      a_off[i] = (uint32_t)(((int64_t)k * p.lda + m0 + cc * 8) * 2);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    if constexpr (!BMN) {
+      const int r = (i * 4 + wave) * RPI + lane / CPR;
+      const int c = kswz<BK>(r, lane % CPR);
+      int64_t row;
+      if (Tr::split) row = r < BN / 2 ? n0 + r : p.I + n0 + (r - BN / 2);
+      else row = n0 + r;
+      b_off[i] = (uint32_t)((row * p.ldb + c * 8) * 2);
+    } else {
+      constexpr int CPRM = BN / 8;
+      const int f = (i * 4 + wave) * 64 + lane;
+      const int k = f / CPRM, cc = (f % CPRM) ^ ((k & 3) << 2);
+      b_off[i] = (uint32_t)(((int64_t)k * p.ldb + n0 + cc * 8) * 2);
+    }
+  }
+  const uint32_t a_kstep = AMN ? (uint32_t)(BK * p.lda * 2) : (uint32_t)(BK * 2);
+  const uint32_t b_kstep = BMN ? (uint32_t)(BK * p.ldb * 2) : (uint32_t)(BK * 2);
+
+  auto issue = [&](int kt, int slot) {
+    const uint32_t sa = lds_base + slot * STAGE;
+    const uint32_t sb = sa + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) dma16(ra, a_off[i] + kt * a_kstep, sa + (i * 4 + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) dma16(rb, b_off[i] + kt * b_kstep, sb + (i * 4 + wave) * 1024);
+  };
+
+  // ---- fragments ----------------------------------------------------------------------------------
+  // LDS row (K-major) or column (MN-major) of the wave's sub-tile j of B.
+  auto b_row = [&](int j) {
+    if (Tr::split) return (j / (TN / 2)) * (BN / 2) + wn * (WTN / 2) + (j % (TN / 2)) * 32;
+    return wn * WTN + j * 32;
+  };
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int grp = lane >> 4, li = lane & 15;
+  auto frag_k = [&](int base, int row0, int kk) -> bf16x8_t {
+    const int r = row0 + l32;
+    return *reinterpret_cast<const bf16x8_t*>(smem + base + r * (BK * 2) +
+                                              kswz<BK>(r, 2 * kk + hi) * 16);
+  };
+  // MN-major: two transposed 8-byte reads give columns col0 + (grp&1)*16 + li,
+  // k = kk*16 + (grp>>1)*8 + 0..7.
+  auto frag_t = [&](int base, int rows, int col0, int kk) -> bf16x8_t {
+    const int col = col0 + (grp & 1) * 16 + 4 * (li & 3);
+    const int cc = col >> 3, half = ((col >> 2) & 1) * 8;
+    const int k0 = kk * 16 + (grp >> 1) * 8 + (li >> 2);
+    const int ad0 = base + k0 * rows * 2 + ((cc ^ ((k0 & 3) << 2)) * 16) + half;
+    const int k1 = k0 + 4;
+    const int ad1 = base + k1 * rows * 2 + ((cc ^ ((k1 & 3) << 2)) * 16) + half;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(s3 + ad0));
+    const v4i16_t hi2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(s3 + ad1));
+    bf16x8_t r;
+    __builtin_memcpy(&r, &lo, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi2, 8);
+    return r;
+  };
+  struct Frags { bf16x8_t a[TM], b[TN]; };
+  auto load = [&](int slot, int kk, Frags& f) {
+    const int sa = slot * STAGE, sb = sa + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (AMN) f.a[i] = frag_t(sa, BM, wm * WTM + i * 32, kk);
+      else f.a[i] = frag_k(sa, wm * WTM + i * 32, kk);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (BMN) f.b[j] = frag_t(sb, BN, b_row(j), kk);
+      else f.b[j] = frag_k(sb, b_row(j), kk);
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = Mf::run(f.b[j], f.a[i], acc[i][j]);
+  };
+
+  // ---- main loop ----------------------------------------------------------------------------------
+  const int nk = (klen + BK - 1) / BK;
+  if (nk > 0) {
+#pragma unroll
+    for (int s0 = 0; s0 < STAGES; ++s0)
+      if (s0 < nk) issue(s0, s0);
+    wait_stages<LA + LB, STAGES - 1>(min(STAGES - 1, nk - 1));
+    block_barrier();
+    Frags cur;
+    load(0, 0, cur);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int slot = kt % STAGES;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        Frags nxt;
+        if (kk + 1 < KK) {
+          load(slot, kk + 1, nxt);
+        } else if (kt + 1 < nk) {
+          // Stage kt + 1 must have landed (own DMA: wait; other waves': the barrier) and every
+          // wave must be done reading this slot before it is refilled.
+          wait_stages<LA + LB, STAGES - 1>(min(STAGES - 2, nk - kt - 2));
+          wait_lgkm0();
+          block_barrier();
+          load((kt + 1) % STAGES, 0, nxt);
+          if (kt + STAGES < nk) issue(kt + STAGES, slot);
+        }
+        mma(cur);
+        cur = nxt;
+      }
+    }
+  }
+
+  store_tile<KIND, TM, TN, WTM, WTN>(p, acc, g, m0, n0, wm, wn, lane);
 }
 
-// Row-grouped kinds with block_m a multiple of 128: tiles of up to kTallRows rows per group.
+// Tile shapes per kind. Row-grouped kinds: one tile shape per height (128, 256, 384 rows),
+// 4 x 1 waves over 128 columns; gate/up takes 64 gate + 64 up columns per tile.
+template <int KIND, int ROWS> struct TallTile { typedef Tile<ROWS, 128, 4, 32> type; };
+constexpr int kTallBN = 128;
+typedef Tile<64, 256, 2, 64> Block64Tile;
+typedef Tile<256, 256, 2, 32> WgradTile;
+
+// Columns of output one tile covers (gate/up: gate columns; the tile also covers as many up).
+template <int KIND> constexpr int tile_cols(int bn) { return KindTraits<KIND>::split ? bn / 2 : bn; }
+
+// ------------------------------------------------------------------------------------------------
+// Eight-wavefront engine (two wavefronts per SIMD) for the tall row-grouped tiles: BK = 64, two
+// LDS stages. A stage's DMA (128-byte row segments, the request size the texture path serves
+// best) is spread over the MFMAs of the slices before the stage is needed: the half of it that
+// fits is issued right after the barrier that frees its slot, the rest during the next two
+// slices, so a wavefront held up at DMA issue leaves the matrix unit to the other wavefront of
+// its SIMD, and the last DMA of a stage still has two slices of MFMAs to land. Fragments are
+// read from LDS at the start of each 16-k slice; the other wavefront's MFMAs cover the latency.
+// ------------------------------------------------------------------------------------------------
+template <int BM_, int BN_, int WM_, int WN_>
+struct Tile8 {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = 8, BK = 64, KK = 4;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
+  static constexpr int LA = A_BYTES / (NW * 1024), LB = B_BYTES / (NW * 1024), L = LA + LB;
+  // DMA instructions of a stage issued after the freeing barrier / in slice 0 / in slice 1
+  static constexpr int P1 = (L + 2) / 3, P2 = (2 * L + 2) / 3;
+  static_assert(WM * WN == NW && TM * 32 == WTM && TN * 32 == WTN, "wave tiling");
+  static_assert(A_BYTES % (NW * 1024) == 0 && B_BYTES % (NW * 1024) == 0, "whole DMA rounds");
+  static_assert(2 * STAGE <= kLdsBytes, "two stages must fit in LDS");
+};
+constexpr int kThreads8 = 512;
+
+template <int KIND, class TL>
+__device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* smem, int g, int m0,
+                                           int n0, int kbeg, int klen) {
+  typedef KindTraits<KIND> Tr;
+  typedef Mfma<32> Mf;
+  constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, WTM = TL::WTM, WTN = TL::WTN;
+  constexpr int TM = TL::TM, TN = TL::TN, NW = TL::NW;
+  constexpr int A_BYTES = TL::A_BYTES, STAGE = TL::STAGE, LA = TL::LA, L = TL::L;
+  constexpr bool AMN = Tr::a_trans, BMN = Tr::b_trans;
+  static_assert(!Tr::split || TN % 2 == 0, "split needs gate and up sub-tiles in pairs");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = (int)uniform((uint32_t)(tid >> 6));
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
+  lds_u8_t* s3 = (lds_u8_t*)smem;
+
+  v4u32_t ra, rb;
+  if (AMN) ra = make_rsrc(p.a + (int64_t)kbeg * p.lda, (int64_t)klen * p.lda * 2);
+  else ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)BM * p.lda * 2);
+  if (Tr::grouped_rows) rb = make_rsrc(p.b + (int64_t)g * p.b_gstride, p.b_gstride * 2);
+  else rb = make_rsrc(p.b + (int64_t)kbeg * p.ldb, (int64_t)klen * p.ldb * 2);
+
+  // ---- DMA addressing: one lane offset per operand; instruction i adds a wave-uniform stride ----
+  // K-major: instruction i of wave w fills rows (i*NW + w)*8 .. +8 (8 lanes per 128-byte row).
+  // MN-major: instruction i of wave w fills flat chunks (i*NW + w)*64 + lane of [BK][ROWS].
+  constexpr int CPR = BK / 8, RPI = 64 / CPR;
+  uint32_t a_off0, b_off0;
+  if constexpr (!AMN) {
+    const int r = wave * RPI + lane / CPR;
+    a_off0 = (uint32_t)(((int64_t)r * p.lda + kswz<BK>(r, lane % CPR) * 8) * 2);
+  } else {
+    constexpr int CPRM = BM / 8;
+    static_assert((64 * NW) % (4 * CPRM) == 0, "instruction stride must keep k & 3");
+    const int f = wave * 64 + lane, k = f / CPRM, cc = (f % CPRM) ^ ((k & 3) << 2);
+    a_off0 = (uint32_t)(((int64_t)k * p.lda + m0 + cc * 8) * 2);
+  }
+  if constexpr (!BMN) {
+    const int r = wave * RPI + lane / CPR;
+    b_off0 = (uint32_t)(((int64_t)(n0 + r) * p.ldb + kswz<BK>(r, lane % CPR) * 8) * 2);
+  } else {
+    constexpr int CPRM = BN / 8;
+    static_assert((64 * NW) % (4 * CPRM) == 0, "instruction stride must keep k & 3");
+    const int f = wave * 64 + lane, k = f / CPRM, cc = (f % CPRM) ^ ((k & 3) << 2);
+    b_off0 = (uint32_t)(((int64_t)k * p.ldb + n0 + cc * 8) * 2);
+  }
+  // byte stride of instruction i within the stage (wave-uniform)
+  auto a_istride = [&](int i) -> uint32_t {
+    if constexpr (!AMN) return (uint32_t)((int64_t)i * NW * RPI * p.lda * 2);
+    else return (uint32_t)((int64_t)i * (64 * NW / (BM / 8)) * p.lda * 2);
+  };
+  auto b_istride = [&](int i) -> uint32_t {
+    if constexpr (!BMN) {
+      int64_t row = (int64_t)i * NW * RPI;
+      if (Tr::split && row >= BN / 2) row += p.I - BN / 2;   // up rows follow the gate rows
+      return (uint32_t)(row * p.ldb * 2);
+    } else {
+      return (uint32_t)((int64_t)i * (64 * NW / (BN / 8)) * p.ldb * 2);
+    }
+  };
+  const uint32_t a_kstep = AMN ? (uint32_t)(BK * p.lda * 2) : (uint32_t)(BK * 2);
+  const uint32_t b_kstep = BMN ? (uint32_t)(BK * p.ldb * 2) : (uint32_t)(BK * 2);
+  // DMA instruction d (0..L-1) of stage kt into slot
+  auto dma_one = [&](int d, int kt, int slot) {
+    const uint32_t sl = lds_base + slot * STAGE;
+    if (d < LA) {
+      dma16(ra, a_off0 + uniform(kt * a_kstep + a_istride(d)), sl + (d * NW + wave) * 1024);
+    } else {
+      const int i = d - LA;
+      dma16(rb, b_off0 + uniform(kt * b_kstep + b_istride(i)), sl + A_BYTES + (i * NW + wave) * 1024);
+    }
+  };
+
+  // ---- fragments -----------------------------------------------------------------------------------
+  auto b_row = [&](int j) {
+    if (Tr::split) return (j / (TN / 2)) * (BN / 2) + wn * (WTN / 2) + (j % (TN / 2)) * 32;
+    return wn * WTN + j * 32;
+  };
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int grp = lane >> 4, li = lane & 15;
+  auto frag_k = [&](int base, int row0, int kk) -> bf16x8_t {
+    const int r = row0 + l32;
+    return *reinterpret_cast<const bf16x8_t*>(smem + base + r * (BK * 2) +
+                                              kswz<BK>(r, 2 * kk + hi) * 16);
+  };
+  auto frag_t = [&](int base, int rows, int col0, int kk) -> bf16x8_t {
+    const int col = col0 + (grp & 1) * 16 + 4 * (li & 3);
+    const int cc = col >> 3, half = ((col >> 2) & 1) * 8;
+    const int k0 = kk * 16 + (grp >> 1) * 8 + (li >> 2);
+    const int ad0 = base + k0 * rows * 2 + ((cc ^ ((k0 & 3) << 2)) * 16) + half;
+    const int k1 = k0 + 4;
+    const int ad1 = base + k1 * rows * 2 + ((cc ^ ((k1 & 3) << 2)) * 16) + half;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(s3 + ad0));
+    const v4i16_t hi2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(s3 + ad1));
+    bf16x8_t r;
+    __builtin_memcpy(&r, &lo, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi2, 8);
+    return r;
+  };
+  struct Frags { bf16x8_t a[TM], b[TN]; };
+  auto load = [&](int slot, int kk, Frags& f) {
+    const int sa = slot * STAGE, sb = sa + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (AMN) f.a[i] = frag_t(sa, BM, wm * WTM + i * 32, kk);
+      else f.a[i] = frag_k(sa, wm * WTM + i * 32, kk);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (BMN) f.b[j] = frag_t(sb, BN, b_row(j), kk);
+      else f.b[j] = frag_k(sb, b_row(j), kk);
+    }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  // The slice's MFMAs with DMA instructions [D0, D1) of stage kt_dma spread evenly among them.
+  auto mma_dma = [&](const Frags& f, auto d0c, auto d1c, bool on, int kt_dma, int slot_dma) {
+    constexpr int D0 = decltype(d0c)::value, D1 = decltype(d1c)::value, N = D1 - D0;
+    constexpr int T = TM * TN;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      acc[t / TN][t % TN] = Mf::run(f.b[t % TN], f.a[t / TN], acc[t / TN][t % TN]);
+      if constexpr (N > 0) {
+#pragma unroll
+        for (int d = 0; d < N; ++d)
+          if (t == (d + 1) * T / (N + 1) - 1 && on) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_one(D0 + d, kt_dma, slot_dma);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+    }
+  };
+  typedef std::integral_constant<int, 0> C0;
+  typedef std::integral_constant<int, TL::P1> CP1;
+  typedef std::integral_constant<int, TL::P2> CP2;
+  typedef std::integral_constant<int, L> CL;
+
+  // ---- main loop: stage kt in slot kt & 1 ---------------------------------------------------------
+  const int nk = (klen + BK - 1) / BK;
+  if (nk > 0) {
+#pragma unroll
+    for (int d = 0; d < L; ++d) dma_one(d, 0, 0);
+    if (nk > 1) {
+#pragma unroll
+      for (int d = 0; d < L; ++d) dma_one(d, 1, 1);
+      wait_vm<L>();
+    } else {
+      wait_vm<0>();
+    }
+    block_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int slot = kt & 1;
+      const bool pend = kt >= 1 && kt + 1 < nk;   // stage kt + 1 still has DMA to issue
+      const bool refill = kt + 2 < nk;            // stage kt + 2 goes into this slot
+      Frags f;
+      load(slot, 0, f);
+      mma_dma(f, CP1(), CP2(), pend, kt + 1, slot ^ 1);
+      load(slot, 1, f);
+      mma_dma(f, CP2(), CL(), pend, kt + 1, slot ^ 1);
+      load(slot, 2, f);
+      mma_dma(f, C0(), C0(), false, 0, 0);
+      load(slot, 3, f);
+      if (kt + 1 < nk) {
+        // This wave's DMA of stage kt + 1 has landed and its reads of this slot are done; the
+        // barrier makes both true for every wave, so stage kt + 1 is visible and the slot free.
+        wait_vm<0>();
+        wait_lgkm0();
+        block_barrier();
+      }
+      mma_dma(f, C0(), CP1(), refill, kt + 2, slot);
+    }
+  }
+  store_tile<KIND, TM, TN, WTM, WTN>(p, acc, g, m0, n0, wm, wn, lane);
+}
+
+// Tall tiles on the eight-wavefront engine: 4 x 2 wavefronts over 256 columns (128 for the
+// dgrad of the down projection, whose SwiGLU-backward epilogue needs the registers and whose
+// I columns are a multiple of 128 but not of 256).
+template <int KIND> constexpr int tall8_bn() { return KIND == kDgradDown ? 128 : 256; }
+template <int KIND, int ROWS> struct Tall8 { typedef Tile8<ROWS, tall8_bn<KIND>(), 4, 2> type; };
+
 template <int KIND>
-__global__ __launch_bounds__(kThreads, 1) void ggemm_tall_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
   int* pref = reinterpret_cast<int*>(smem);   // tiles before group g (reused by the DMA ring)
   const int tid = threadIdx.x, lane = tid & 63;
@@ -741,8 +947,8 @@ __global__ __launch_bounds__(kThreads, 1) void ggemm_tall_kernel(GemmArgs p) {
     int run = 0;
     for (int base = 0; base < G; base += 64) {
       const int g = base + lane;
-      const int len = g < G ? p.seg[g + 1] - p.seg[g] : 0;
-      int x = (len + kTallRows - 1) / kTallRows;
+      const int nb = g < G ? (p.seg[g + 1] - p.seg[g]) / kTallBlk : 0;
+      int x = (nb + kTallMaxBlk - 1) / kTallMaxBlk;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(x, o, 64);
@@ -756,49 +962,109 @@ __global__ __launch_bounds__(kThreads, 1) void ggemm_tall_kernel(GemmArgs p) {
   __syncthreads();
   const int64_t n_tiles = pref[G];
   const int64_t L = xcd_remap(blockIdx.x, n_tiles * p.n_tiles_n);
-  if (L < 0) return;
-  const int ti = (int)(L / p.n_tiles_n), nt = (int)(L % p.n_tiles_n);
-  int lo = 0, hi = G - 1;   // group of tile ti: largest g with pref[g] <= ti
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pref[mid] <= ti) lo = mid; else hi = mid - 1;
+  int g = 0, ti = 0, nt = 0;
+  if (L >= 0) {
+    ti = (int)(L / p.n_tiles_n);
+    nt = (int)(L % p.n_tiles_n);
+    int lo = 0, hi = G - 1;   // group of tile ti: largest g with pref[g] <= ti
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pref[mid] <= ti) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
   }
-  const int g = lo;
-  const int m0 = p.seg[g] + (ti - pref[g]) * kTallRows;
-  const int rows = min(kTallRows, p.seg[g + 1] - m0);
-  const int n0 = nt * (KindTraits<KIND>::split ? DmaCfg<128>::BN / 2 : DmaCfg<128>::BN);
+  const int t0 = pref[g], ntg = pref[g + 1] - t0;
   __syncthreads();   // pref is dead from here on: the DMA ring may overwrite it
-  const uint32_t lb = lds_addr_of(smem);
-  if (rows == 256) dma_tile<KIND, 256>(p, smem, lb, g, m0, n0, 0, p.K);
-  else dma_tile<KIND, 128>(p, smem, lb, g, m0, n0, 0, p.K);
+  if (L < 0) return;
+  const int nb = (p.seg[g + 1] - p.seg[g]) / kTallBlk;
+  const int local = ti - t0, base = nb / ntg, extra = nb % ntg;
+  const int blk0 = local * base + min(local, extra), nblk = base + (local < extra ? 1 : 0);
+  const int m0 = p.seg[g] + blk0 * kTallBlk;
+  const int n0 = nt * tile_cols<KIND>(tall8_bn<KIND>());
+  if (nblk == 3) pipe8_tile<KIND, typename Tall8<KIND, 384>::type>(p, smem, g, m0, n0, 0, p.K);
+  else if (nblk == 2) pipe8_tile<KIND, typename Tall8<KIND, 256>::type>(p, smem, g, m0, n0, 0, p.K);
+  else pipe8_tile<KIND, typename Tall8<KIND, 128>::type>(p, smem, g, m0, n0, 0, p.K);
+}
+
+// Row-grouped kinds with block_m a multiple of 128: every segment is cut into ceil(blocks / 3)
+// tiles of 1 to 3 whole 128-row blocks (the first `extra` tiles one block taller).
+template <int KIND>
+__global__ __launch_bounds__(kThreads, 1) void ggemm_tall_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
+  int* pref = reinterpret_cast<int*>(smem);   // tiles before group g (reused by the DMA ring)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int G = p.G;
+  if (tid < 64) {
+    int run = 0;
+    for (int base = 0; base < G; base += 64) {
+      const int g = base + lane;
+      const int nb = g < G ? (p.seg[g + 1] - p.seg[g]) / kTallBlk : 0;
+      int x = (nb + kTallMaxBlk - 1) / kTallMaxBlk;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (g < G) pref[g + 1] = run + x;
+      run += __shfl(x, 63, 64);
+    }
+    if (lane == 0) pref[0] = 0;
+  }
+  __syncthreads();
+  const int64_t n_tiles = pref[G];
+  const int64_t L = xcd_remap(blockIdx.x, n_tiles * p.n_tiles_n);
+  int g = 0, ti = 0, nt = 0;
+  if (L >= 0) {
+    ti = (int)(L / p.n_tiles_n);
+    nt = (int)(L % p.n_tiles_n);
+    int lo = 0, hi = G - 1;   // group of tile ti: largest g with pref[g] <= ti
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pref[mid] <= ti) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+  }
+  const int t0 = pref[g], ntg = pref[g + 1] - t0;
+  __syncthreads();   // pref is dead from here on: the DMA ring may overwrite it
+  if (L < 0) return;
+  const int nb = (p.seg[g + 1] - p.seg[g]) / kTallBlk;
+  const int local = ti - t0, base = nb / ntg, extra = nb % ntg;
+  const int blk0 = local * base + min(local, extra), nblk = base + (local < extra ? 1 : 0);
+  const int m0 = p.seg[g] + blk0 * kTallBlk;
+  const int n0 = nt * tile_cols<KIND>(kTallBN);
+  if (nblk == 3) pipe_tile<KIND, typename TallTile<KIND, 384>::type>(p, smem, g, m0, n0, 0, p.K);
+  else if (nblk == 2) pipe_tile<KIND, typename TallTile<KIND, 256>::type>(p, smem, g, m0, n0, 0, p.K);
+  else pipe_tile<KIND, typename TallTile<KIND, 128>::type>(p, smem, g, m0, n0, 0, p.K);
 }
 
 // Row-grouped kinds with 64-row tiles (block_m == 64): one block per tile, from tile_group.
 template <int KIND>
 __global__ __launch_bounds__(kThreads, 1) void ggemm_block64_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[DmaCfg<64>::STAGES * DmaCfg<64>::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Block64Tile::STAGES * Block64Tile::STAGE];
   const int total = p.total_rows[0];
   const int64_t L = xcd_remap(blockIdx.x, (int64_t)(total / 64) * p.n_tiles_n);
   if (L < 0) return;
   const int mt = (int)(L / p.n_tiles_n), nt = (int)(L % p.n_tiles_n);
   const int m0 = mt * 64;
   const int g = p.tile_group[m0 / p.block_m];
-  const int n0 = nt * (KindTraits<KIND>::split ? DmaCfg<64>::BN / 2 : DmaCfg<64>::BN);
-  dma_tile<KIND, 64>(p, smem, lds_addr_of(smem), g, m0, n0, 0, p.K);
+  const int n0 = nt * tile_cols<KIND>(Block64Tile::BN);
+  pipe_tile<KIND, Block64Tile>(p, smem, g, m0, n0, 0, p.K);
 }
 
-// Weight-gradient kinds: 256 weight rows x 256 columns per tile, contraction over the segment.
+// Weight-gradient kinds on the eight-wavefront engine: 256 weight rows x 256 columns per tile,
+// contraction over the segment's rows (both operands MN-major in HBM).
+typedef Tile8<256, 256, 4, 2> Wgrad8Tile;
 template <int KIND>
-__global__ __launch_bounds__(kThreads, 1) void ggemm_wgrad_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[DmaCfg<256>::STAGES * DmaCfg<256>::STAGE];
+__global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * Wgrad8Tile::STAGE];
   const int64_t per_g = (int64_t)p.n_tiles_m * p.n_tiles_n;
   const int64_t L = xcd_remap(blockIdx.x, per_g * p.G);
   if (L < 0) return;
   const int g = (int)(L / per_g);
   const int rem = (int)(L % per_g);
-  const int m0 = (rem / p.n_tiles_n) * 256, n0 = (rem % p.n_tiles_n) * 256;
+  const int m0 = (rem / p.n_tiles_n) * Wgrad8Tile::BM, n0 = (rem % p.n_tiles_n) * Wgrad8Tile::BN;
   const int kbeg = p.seg[g], klen = p.seg[g + 1] - kbeg;
-  dma_tile<KIND, 256>(p, smem, lds_addr_of(smem), g, m0, n0, kbeg, klen);
+  pipe8_tile<KIND, Wgrad8Tile>(p, smem, g, m0, n0, kbeg, klen);
 }
 
 template <int KIND, int BM, int BN, int MS, int WAVES_M>
@@ -809,27 +1075,31 @@ hipError_t launch_kind(const GemmArgs& a, int64_t grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Row-grouped kinds: pick the tile height from block_m (it must divide block_m).
+// Row-grouped kinds: tall tiles for block_m % 128 == 0, 64-row tiles for block_m == 64, the
+// register-staged engine for 16 and 32.
 template <int KIND>
-hipError_t launch_rows(GemmArgs a, int64_t mcap, int n_per_tile, hipStream_t st) {
-  const int bm = a.block_m >= 128 ? 128 : a.block_m;
-  a.n_tiles_n = (int)((a.N + n_per_tile - 1) / n_per_tile);
-  const int64_t tiles = (mcap / bm) * a.n_tiles_n;
-  const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
-  if (a.block_m % 128 == 0) {
-    if (a.seg == nullptr || a.total_rows == nullptr) return hipErrorInvalidValue;
-    // Tall tiles: at most mcap/256 + G tiles (each group adds at most one short tile).
-    const int64_t tall = (mcap / kTallRows + a.G) * a.n_tiles_n;
-    const int64_t g2 = (tall + kNumXcd - 1) / kNumXcd * kNumXcd;
-    hipLaunchKernelGGL((ggemm_tall_kernel<KIND>), dim3((unsigned)g2), dim3(kThreads), 0, st, a);
+hipError_t launch_rows(GemmArgs a, int64_t mcap, hipStream_t st) {
+  if (a.block_m % kTallBlk == 0) {
+    if (a.seg == nullptr) return hipErrorInvalidValue;
+    constexpr int cols = tile_cols<KIND>(tall8_bn<KIND>());
+    a.n_tiles_n = (int)((a.N + cols - 1) / cols);
+    // sum over groups of ceil(nb_g / 3) <= (sum nb_g + 2 G) / 3, sum nb_g <= mcap / 128
+    const int64_t tiles = (mcap / kTallBlk + 2 * (int64_t)a.G) / kTallMaxBlk + 1;
+    const int64_t grid = (tiles * a.n_tiles_n + kNumXcd - 1) / kNumXcd * kNumXcd;
+    hipLaunchKernelGGL((ggemm_tall8_kernel<KIND>), dim3((unsigned)grid), dim3(kThreads8), 0, st, a);
     return hipGetLastError();
   }
   if (a.tile_group == nullptr || a.total_rows == nullptr) return hipErrorInvalidValue;
   if (a.block_m == 64) {
+    a.n_tiles_n = (int)((a.N + tile_cols<KIND>(Block64Tile::BN) - 1) / tile_cols<KIND>(Block64Tile::BN));
+    const int64_t grid = ((mcap / 64) * a.n_tiles_n + kNumXcd - 1) / kNumXcd * kNumXcd;
     hipLaunchKernelGGL((ggemm_block64_kernel<KIND>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
   }
-  switch (bm) {
+  const int n_per_tile = KindTraits<KIND>::split ? 128 : 256;
+  a.n_tiles_n = (int)((a.N + n_per_tile - 1) / n_per_tile);
+  const int64_t grid = ((mcap / a.block_m) * a.n_tiles_n + kNumXcd - 1) / kNumXcd * kNumXcd;
+  switch (a.block_m) {
     case 32: return launch_kind<KIND, 32, 256, 32, 1>(a, grid, st);
     case 16: return launch_kind<KIND, 16, 256, 16, 1>(a, grid, st);
     default: return hipErrorInvalidValue;
@@ -856,7 +1126,7 @@ hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
   g.out = a; g.ldo = s.I; g.out2 = h_save;
   g.N = s.I; g.K = s.H;
   if (which & MOE_FWD_GATEUP) {
-    hipError_t e = launch_rows<kFwdGateUp>(g, mcap, 128, st);
+    hipError_t e = launch_rows<kFwdGateUp>(g, mcap, st);
     if (e != hipSuccess) return e;
   }
   if (!(which & MOE_FWD_DOWN)) return hipSuccess;
@@ -865,7 +1135,7 @@ hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
   g.b = w2; g.ldb = s.I; g.b_gstride = (int64_t)s.H * s.I;
   g.out = y_perm; g.ldo = s.H; g.out2 = nullptr;
   g.N = s.H; g.K = s.I;
-  return launch_rows<kFwdDown>(g, mcap, 256, st);
+  return launch_rows<kFwdDown>(g, mcap, st);
 }
 
 hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap,
@@ -886,7 +1156,7 @@ hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap
   g.aux = h_save; g.out = dh;
   g.N = s.I; g.K = s.H;
   if (which & MOE_DGRAD_DOWN) {
-    hipError_t e = launch_rows<kDgradDown>(g, mcap, 256, st);
+    hipError_t e = launch_rows<kDgradDown>(g, mcap, st);
     if (e != hipSuccess) return e;
   }
   if (!(which & MOE_DGRAD_GATEUP)) return hipSuccess;
@@ -895,7 +1165,7 @@ hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap
   g.b = w1; g.ldb = s.H; g.b_gstride = (int64_t)2 * s.I * s.H;
   g.aux = nullptr; g.out = dx_perm; g.ldo = s.H;
   g.N = s.H; g.K = 2 * s.I;
-  return launch_rows<kDgradGateUp>(g, mcap, 256, st);
+  return launch_rows<kDgradGateUp>(g, mcap, st);
 }
 
 hipError_t launch_ggemm_wgrad(const moe_shape_t& s, uint32_t which, const uint16_t* x_perm,
@@ -912,12 +1182,12 @@ hipError_t launch_ggemm_wgrad(const moe_shape_t& s, uint32_t which, const uint16
   g.b = a; g.ldb = s.I;
   g.out = dw2; g.ldo = s.I; g.o_gstride = (int64_t)s.H * s.I;
   g.M = s.H; g.N = s.I;
-  g.n_tiles_m = (g.M + 255) / 256;
-  g.n_tiles_n = (g.N + 255) / 256;
+  g.n_tiles_m = (g.M + Wgrad8Tile::BM - 1) / Wgrad8Tile::BM;
+  g.n_tiles_n = (g.N + Wgrad8Tile::BN - 1) / Wgrad8Tile::BN;
   int64_t tiles = (int64_t)g.G * g.n_tiles_m * g.n_tiles_n;
   if (which & MOE_WGRAD_DOWN) {
-    hipLaunchKernelGGL((ggemm_wgrad_kernel<kWgradDown>),
-                       dim3((unsigned)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd)), dim3(kThreads),
+    hipLaunchKernelGGL((ggemm_wgrad8_kernel<kWgradDown>),
+                       dim3((unsigned)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd)), dim3(kThreads8),
                        0, st, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -928,11 +1198,11 @@ hipError_t launch_ggemm_wgrad(const moe_shape_t& s, uint32_t which, const uint16
   g.b = x_perm; g.ldb = s.H;
   g.out = dw1; g.ldo = s.H; g.o_gstride = (int64_t)2 * s.I * s.H;
   g.M = 2 * s.I; g.N = s.H;
-  g.n_tiles_m = (g.M + 255) / 256;
-  g.n_tiles_n = (g.N + 255) / 256;
+  g.n_tiles_m = (g.M + Wgrad8Tile::BM - 1) / Wgrad8Tile::BM;
+  g.n_tiles_n = (g.N + Wgrad8Tile::BN - 1) / Wgrad8Tile::BN;
   tiles = (int64_t)g.G * g.n_tiles_m * g.n_tiles_n;
-  hipLaunchKernelGGL((ggemm_wgrad_kernel<kWgradGateUp>),
-                     dim3((unsigned)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((ggemm_wgrad8_kernel<kWgradGateUp>),
+                     dim3((unsigned)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd)), dim3(kThreads8), 0,
                      st, g);
   return hipGetLastError();
 }
