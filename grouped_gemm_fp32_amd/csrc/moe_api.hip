@@ -66,6 +66,17 @@ int64_t capacity(const moe_shape_t* s) {
     }                                                             \
   } while (0)
 
+// A bf16 tensor the grouped GEMMs read or write: non-NULL and 16-byte aligned (the kernels move
+// 16-byte chunks).
+#define REQUIRE_T(p)                                                   \
+  do {                                                                 \
+    REQUIRE(p);                                                        \
+    if ((uintptr_t)(p) % 16 != 0) {                                    \
+      set_err("tensor pointer is not 16-byte aligned: " #p);           \
+      return MOE_ERR_INVALID_ARG;                                      \
+    }                                                                  \
+  } while (0)
+
 #define CHECK_SHAPE(s)                       \
   do {                                       \
     moe_status_t st_ = check_shape(s);       \
@@ -164,14 +175,15 @@ moe_status_t grouped_gemm_fwd(const moe_shape_t* s, uint32_t which, const uint16
   REQUIRE(seg_offsets);
   REQUIRE(tile_group);
   REQUIRE(total_rows);
-  REQUIRE(a);
+  REQUIRE_T(a);
+  if (h_save) REQUIRE_T(h_save);
   if (which & MOE_FWD_GATEUP) {
-    REQUIRE(x_perm);
-    REQUIRE(w1);
+    REQUIRE_T(x_perm);
+    REQUIRE_T(w1);
   }
   if (which & MOE_FWD_DOWN) {
-    REQUIRE(w2);
-    REQUIRE(y_perm);
+    REQUIRE_T(w2);
+    REQUIRE_T(y_perm);
   }
   return hip_status(moe::launch_ggemm_fwd(*s, which, capacity(s), x_perm, seg_offsets, tile_group, total_rows,
                                           w1, w2, h_save, a, y_perm, (hipStream_t)stream),
@@ -194,30 +206,30 @@ moe_status_t grouped_gemm_bwd(const moe_shape_t* s, uint32_t which, const uint16
     REQUIRE(seg_offsets);
     REQUIRE(tile_group);
     REQUIRE(total_rows);
-    REQUIRE(dh);
+    REQUIRE_T(dh);
   }
   if (rows && (which & MOE_DGRAD_DOWN)) {
-    REQUIRE(dy_perm);
-    REQUIRE(h_save);
-    REQUIRE(w2);
+    REQUIRE_T(dy_perm);
+    REQUIRE_T(h_save);
+    REQUIRE_T(w2);
   }
   if (rows && (which & MOE_DGRAD_GATEUP)) {
-    REQUIRE(w1);
-    REQUIRE(dx_perm);
+    REQUIRE_T(w1);
+    REQUIRE_T(dx_perm);
   }
   if (which & MOE_WGRAD) REQUIRE(seg_offsets);
   if (which & MOE_WGRAD_DOWN) {
-    REQUIRE(dw2);
+    REQUIRE_T(dw2);
     if (rows) {
-      REQUIRE(dy_perm);
-      REQUIRE(a);
+      REQUIRE_T(dy_perm);
+      REQUIRE_T(a);
     }
   }
   if (which & MOE_WGRAD_GATEUP) {
-    REQUIRE(dw1);
+    REQUIRE_T(dw1);
     if (rows) {
-      REQUIRE(dh);
-      REQUIRE(x_perm);
+      REQUIRE_T(dh);
+      REQUIRE_T(x_perm);
     }
   }
   hipStream_t st = (hipStream_t)stream;

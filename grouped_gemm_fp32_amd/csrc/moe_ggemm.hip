@@ -727,6 +727,129 @@ typedef Tile<256, 256, 2, 32> WgradTile;
 template <int KIND> constexpr int tile_cols(int bn) { return KindTraits<KIND>::split ? bn / 2 : bn; }
 
 // ------------------------------------------------------------------------------------------------
+// Epilogue of the eight-wavefront engine. An MFMA result gives each lane 4 consecutive columns of
+// one row, so storing straight from registers writes 16 bytes to each of 32 rows per instruction.
+// Instead every 32-row block goes through a per-wavefront LDS buffer (16-byte chunks XOR-swizzled
+// by row) and leaves in 16-byte chunks with a whole 128- or 256-byte row segment per group of
+// lanes.
+// ------------------------------------------------------------------------------------------------
+// Stage a 32 x (NJ*32) block of bf16 values (val(j, q, e): sub-tile j, column group q, element e of
+// this lane's row) and hand each 16-byte row chunk to dst(row, col, uint4).
+template <int NJ, class Val, class Dst>
+__device__ __forceinline__ void stage_bf16(unsigned char* scr, int lane, Val val, Dst dst) {
+  constexpr int W = NJ * 32, NCH = W / 8, RS = W * 2, RPI = 64 / NCH;
+  static_assert(NCH >= 4 && NCH <= 64 && (NCH & (NCH - 1)) == 0, "row chunks");
+  const int r = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ch = 4 * j + q;
+      const uint2 w = make_uint2(pack_bf2(val(j, q, 0), val(j, q, 1)), pack_bf2(val(j, q, 2), val(j, q, 3)));
+      *reinterpret_cast<uint2*>(scr + r * RS + ((ch ^ (r & (NCH - 1))) * 16) + hi * 8) = w;
+    }
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int rr = it * RPI + lane / NCH, c = lane % NCH;
+    const uint4 d = *reinterpret_cast<const uint4*>(scr + rr * RS + ((c ^ (rr & (NCH - 1))) * 16));
+    dst(rr, c * 8, d);
+  }
+}
+
+// The same for fp32 values: dst(row, col, float4) gets 4 consecutive columns.
+template <int NJ, class Val, class Dst>
+__device__ __forceinline__ void stage_f32(unsigned char* scr, int lane, Val val, Dst dst) {
+  constexpr int W = NJ * 32, NCH = W / 4, RS = W * 4, RPI = 64 / NCH;
+  static_assert(NCH >= 4 && NCH <= 64 && (NCH & (NCH - 1)) == 0, "row chunks");
+  const int r = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ch = 8 * j + 2 * q + hi;
+      const float4 w = make_float4(val(j, q, 0), val(j, q, 1), val(j, q, 2), val(j, q, 3));
+      *reinterpret_cast<float4*>(scr + r * RS + ((ch ^ (r & (NCH - 1))) * 16)) = w;
+    }
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int rr = it * RPI + lane / NCH, c = lane % NCH;
+    const float4 d = *reinterpret_cast<const float4*>(scr + rr * RS + ((c ^ (rr & (NCH - 1))) * 16));
+    dst(rr, c * 4, d);
+  }
+}
+
+__device__ __forceinline__ float4 bf4_to_f4(uint2 w) {
+  return make_float4(lo_bf(w.x), hi_bf(w.x), lo_bf(w.y), hi_bf(w.y));
+}
+
+// scr: this wavefront's LDS buffer of at least 8 KiB.
+template <int KIND, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void store_tile8(const GemmArgs& p, const f32x16_t (&acc)[TM][TN], int g,
+                                            int m0, int n0, int wm, int wn, int lane,
+                                            unsigned char* scr) {
+  typedef KindTraits<KIND> Tr;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t mrow = m0 + wm * WTM + i * 32;   // first row of this 32-row block
+    if constexpr (Tr::split) {
+      // a = silu(gate) * up, columns n0 + wn*WTN/2 .. of [rows, I]; then h = [gate | up] rows.
+      constexpr int NJ = TN / 2;
+      const int c0 = n0 + wn * (WTN / 2);
+      stage_bf16<NJ>(scr, lane,
+          [&](int j, int q, int e) { return silu_f(acc[i][j][4 * q + e]) * acc[i][j + NJ][4 * q + e]; },
+          [&](int rr, int c, uint4 d) {
+            if (c0 + c < p.I) *reinterpret_cast<uint4*>(p.out + (mrow + rr) * p.ldo + c0 + c) = d;
+          });
+      if (p.out2) {
+        uint16_t* h = p.out2;
+        const int64_t ldh = 2 * (int64_t)p.I;
+        stage_bf16<NJ>(scr, lane, [&](int j, int q, int e) { return acc[i][j][4 * q + e]; },
+            [&](int rr, int c, uint4 d) {
+              if (c0 + c < p.I) *reinterpret_cast<uint4*>(h + (mrow + rr) * ldh + c0 + c) = d;
+            });
+        stage_bf16<NJ>(scr, lane, [&](int j, int q, int e) { return acc[i][j + NJ][4 * q + e]; },
+            [&](int rr, int c, uint4 d) {
+              if (c0 + c < p.I) *reinterpret_cast<uint4*>(h + (mrow + rr) * ldh + p.I + c0 + c) = d;
+            });
+      }
+    } else if constexpr (KIND == kDgradDown) {
+      // da (fp32) meets the saved h: dg = da*u*s*(1 + g*(1 - s)), du = da*g*s, s = sigmoid(g).
+      const int c0 = n0 + wn * WTN;
+      const int64_t ldh = 2 * (int64_t)p.I;
+      stage_f32<TN>(scr, lane, [&](int j, int q, int e) { return acc[i][j][4 * q + e]; },
+          [&](int rr, int c, float4 da) {
+            if (c0 + c >= p.N) return;
+            const int64_t hrow = (mrow + rr) * ldh + c0 + c;
+            const float4 gg = bf4_to_f4(*reinterpret_cast<const uint2*>(p.aux + hrow));
+            const float4 uu = bf4_to_f4(*reinterpret_cast<const uint2*>(p.aux + hrow + p.I));
+            const float gv[4] = {gg.x, gg.y, gg.z, gg.w}, uv[4] = {uu.x, uu.y, uu.z, uu.w};
+            const float av[4] = {da.x, da.y, da.z, da.w};
+            float dg[4], du[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sg = 1.0f / (1.0f + expf(-gv[e]));
+              dg[e] = av[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+              du[e] = av[e] * gv[e] * sg;
+            }
+            *reinterpret_cast<uint2*>(p.out + hrow) =
+                make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(p.out + hrow + p.I) =
+                make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+          });
+    } else {
+      uint16_t* out = p.out + (Tr::grouped_rows ? 0 : (int64_t)g * p.o_gstride);
+      const int c0 = n0 + wn * WTN;
+      stage_bf16<TN>(scr, lane, [&](int j, int q, int e) { return acc[i][j][4 * q + e]; },
+          [&](int rr, int c, uint4 d) {
+            const int64_t m = mrow + rr;
+            if (!Tr::grouped_rows && m >= p.M) return;
+            if (c0 + c < p.N) *reinterpret_cast<uint4*>(out + m * p.ldo + c0 + c) = d;
+          });
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // Eight-wavefront engine (two wavefronts per SIMD) for the tall row-grouped tiles: BK = 64, two
 // LDS stages. A stage's DMA (128-byte row segments, the request size the texture path serves
 // best) is spread over the MFMAs of the slices before the stage is needed: the half of it that
@@ -928,7 +1051,11 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
       mma_dma(f, C0(), CP1(), refill, kt + 2, slot);
     }
   }
-  store_tile<KIND, TM, TN, WTM, WTN>(p, acc, g, m0, n0, wm, wn, lane);
+  // Every wavefront is done with the ring: the two stages become per-wavefront staging buffers.
+  static_assert(2 * STAGE / NW >= 8192, "8 KiB of LDS per wavefront for the epilogue");
+  wait_lgkm0();
+  block_barrier();
+  store_tile8<KIND, TM, TN, WTM, WTN>(p, acc, g, m0, n0, wm, wn, lane, smem + wave * (2 * STAGE / NW));
 }
 
 // Tall tiles on the eight-wavefront engine: 4 x 2 wavefronts over 256 columns (128 for the

@@ -20,8 +20,9 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream) and never
  *     synchronises the host. Data-dependent sizes (total_rows, tile_group) stay on the device.
  *   - Arguments are checked on the host before any launch: MOE_ERR_INVALID_ARG for a NULL
- *     required pointer or an impossible shape, MOE_ERR_UNSUPPORTED for shapes the kernels are not
- *     built for, MOE_ERR_WORKSPACE if ws_bytes is too small.
+ *     required pointer, a bf16 tensor of grouped_gemm_fwd/bwd that is not 16-byte aligned, or an
+ *     impossible shape, MOE_ERR_UNSUPPORTED for shapes the kernels are not built for,
+ *     MOE_ERR_WORKSPACE if ws_bytes is too small.
  *   - T == 0 (an empty batch) reads nothing: moe_permute writes seg_offsets = 0 and
  *     total_rows = 0, grouped_gemm_bwd with a WGRAD bit writes zero weight gradients, every other
  *     call is a no-op returning MOE_OK; pointers to T- or Mcap-sized arrays may then be NULL.

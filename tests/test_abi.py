@@ -108,6 +108,21 @@ def test_null_required_pointers(lib):
     assert "NULL" in M.moe_last_error()
 
 
+def test_gemm_tensors_must_be_16_byte_aligned(lib):
+    s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
+    d, odd = ctypes.c_void_p(16), ctypes.c_void_p(16 + 8)
+    for i in (0, 4, 5, 7, 8):   # x_perm, w1, w2, a, y_perm
+        a = [d] * 9
+        a[i] = odd
+        assert lib.grouped_gemm_fwd(ctypes.byref(s), M.MOE_FWD, *a, None) == -1
+        assert "aligned" in M.moe_last_error()
+    for i in (0, 1, 2, 3, 9, 10, 11, 12):   # x_perm, h_save, a, dy_perm, dh, dx_perm, dw1, dw2
+        a = [d] * 13
+        a[i] = odd
+        assert lib.grouped_gemm_bwd(ctypes.byref(s), M.MOE_DGRAD | M.MOE_WGRAD, *a, None) == -1
+        assert "aligned" in M.moe_last_error()
+
+
 def test_workspace_too_small(lib):
     s = M.make_shape(1000, 256, 8, 2, 128, 1, 16)
     need = M.moe_workspace_size(s)
