@@ -872,58 +872,76 @@ struct Tile8 {
 };
 constexpr int kThreads8 = 512;
 
+// The engine proper: DMA addressing of one tile at a time, fragment reads and the pipelined
+// contraction. A persistent kernel may set up the next tile's DMA while the accumulators of the
+// current one are still live.
 template <int KIND, class TL>
-__device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* smem, int g, int m0,
-                                           int n0, int kbeg, int klen) {
+struct Eng8 {
   typedef KindTraits<KIND> Tr;
   typedef Mfma<32> Mf;
-  constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, WTM = TL::WTM, WTN = TL::WTN;
-  constexpr int TM = TL::TM, TN = TL::TN, NW = TL::NW;
-  constexpr int A_BYTES = TL::A_BYTES, STAGE = TL::STAGE, LA = TL::LA, L = TL::L;
-  constexpr bool AMN = Tr::a_trans, BMN = Tr::b_trans;
-  static_assert(!Tr::split || TN % 2 == 0, "split needs gate and up sub-tiles in pairs");
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = (int)uniform((uint32_t)(tid >> 6));
-  const int wm = wave / TL::WN, wn = wave % TL::WN;
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
-  lds_u8_t* s3 = (lds_u8_t*)smem;
-
-  v4u32_t ra, rb;
-  if (AMN) ra = make_rsrc(p.a + (int64_t)kbeg * p.lda, (int64_t)klen * p.lda * 2);
-  else ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)BM * p.lda * 2);
-  if (Tr::grouped_rows) rb = make_rsrc(p.b + (int64_t)g * p.b_gstride, p.b_gstride * 2);
-  else rb = make_rsrc(p.b + (int64_t)kbeg * p.ldb, (int64_t)klen * p.ldb * 2);
-
-  // ---- DMA addressing: one lane offset per operand; instruction i adds a wave-uniform stride ----
-  // K-major: instruction i of wave w fills rows (i*NW + w)*8 .. +8 (8 lanes per 128-byte row).
+  static constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, WTM = TL::WTM, WTN = TL::WTN;
+  static constexpr int TM = TL::TM, TN = TL::TN, NW = TL::NW;
+  static constexpr int A_BYTES = TL::A_BYTES, STAGE = TL::STAGE, LA = TL::LA, L = TL::L;
+  static constexpr bool AMN = Tr::a_trans, BMN = Tr::b_trans;
+  // K-major: instruction i of wave w fills rows (i*NW + w)*RPI .. +RPI (8 lanes per 128-byte row).
   // MN-major: instruction i of wave w fills flat chunks (i*NW + w)*64 + lane of [BK][ROWS].
-  constexpr int CPR = BK / 8, RPI = 64 / CPR;
-  uint32_t a_off0, b_off0;
-  if constexpr (!AMN) {
-    const int r = wave * RPI + lane / CPR;
-    a_off0 = (uint32_t)(((int64_t)r * p.lda + kswz<BK>(r, lane % CPR) * 8) * 2);
-  } else {
-    constexpr int CPRM = BM / 8;
-    static_assert((64 * NW) % (4 * CPRM) == 0, "instruction stride must keep k & 3");
-    const int f = wave * 64 + lane, k = f / CPRM, cc = (f % CPRM) ^ ((k & 3) << 2);
-    a_off0 = (uint32_t)(((int64_t)k * p.lda + m0 + cc * 8) * 2);
+  static constexpr int CPR = BK / 8, RPI = 64 / CPR;
+  static_assert(!Tr::split || TN % 2 == 0, "split needs gate and up sub-tiles in pairs");
+  struct Frags { bf16x8_t a[TM], b[TN]; };
+  typedef f32x16_t Acc[TM][TN];
+
+  const GemmArgs& p;
+  unsigned char* smem;
+  lds_u8_t* s3;
+  uint32_t lds_base;
+  int lane, wave, wm, wn;
+  // DMA state of the tile being loaded: one lane offset per operand, instruction i adds a
+  // wave-uniform stride, stage kt adds kt * kstep.
+  v4u32_t ra, rb;
+  uint32_t a_off0, b_off0, a_kstep, b_kstep;
+
+  __device__ __forceinline__ Eng8(const GemmArgs& p_, unsigned char* smem_) : p(p_), smem(smem_) {
+    s3 = (lds_u8_t*)smem;
+    lds_base = (uint32_t)(uintptr_t)s3;
+    lane = threadIdx.x & 63;
+    wave = (int)uniform((uint32_t)(threadIdx.x >> 6));
+    wm = wave / TL::WN;
+    wn = wave % TL::WN;
+    a_kstep = AMN ? (uint32_t)(BK * p.lda * 2) : (uint32_t)(BK * 2);
+    b_kstep = BMN ? (uint32_t)(BK * p.ldb * 2) : (uint32_t)(BK * 2);
   }
-  if constexpr (!BMN) {
-    const int r = wave * RPI + lane / CPR;
-    b_off0 = (uint32_t)(((int64_t)(n0 + r) * p.ldb + kswz<BK>(r, lane % CPR) * 8) * 2);
-  } else {
-    constexpr int CPRM = BN / 8;
-    static_assert((64 * NW) % (4 * CPRM) == 0, "instruction stride must keep k & 3");
-    const int f = wave * 64 + lane, k = f / CPRM, cc = (f % CPRM) ^ ((k & 3) << 2);
-    b_off0 = (uint32_t)(((int64_t)k * p.ldb + n0 + cc * 8) * 2);
+
+  // Tile: rows m0.. of group g (row-grouped kinds) or weight rows m0.. of group g (wgrad),
+  // columns n0.., contraction over [kbeg, kbeg + klen).
+  __device__ __forceinline__ void setup(int g, int m0, int n0, int kbeg, int klen) {
+    if (AMN) ra = make_rsrc(p.a + (int64_t)kbeg * p.lda, (int64_t)klen * p.lda * 2);
+    else ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)BM * p.lda * 2);
+    if (Tr::grouped_rows) rb = make_rsrc(p.b + (int64_t)g * p.b_gstride, p.b_gstride * 2);
+    else rb = make_rsrc(p.b + (int64_t)kbeg * p.ldb, (int64_t)klen * p.ldb * 2);
+    if constexpr (!AMN) {
+      const int r = wave * RPI + lane / CPR;
+      a_off0 = (uint32_t)(((int64_t)r * p.lda + kswz<BK>(r, lane % CPR) * 8) * 2);
+    } else {
+      constexpr int CPRM = BM / 8;
+      static_assert((64 * NW) % (4 * CPRM) == 0, "instruction stride must keep k & 3");
+      const int f = wave * 64 + lane, k = f / CPRM, cc = (f % CPRM) ^ ((k & 3) << 2);
+      a_off0 = (uint32_t)(((int64_t)k * p.lda + m0 + cc * 8) * 2);
+    }
+    if constexpr (!BMN) {
+      const int r = wave * RPI + lane / CPR;
+      b_off0 = (uint32_t)(((int64_t)(n0 + r) * p.ldb + kswz<BK>(r, lane % CPR) * 8) * 2);
+    } else {
+      constexpr int CPRM = BN / 8;
+      static_assert((64 * NW) % (4 * CPRM) == 0, "instruction stride must keep k & 3");
+      const int f = wave * 64 + lane, k = f / CPRM, cc = (f % CPRM) ^ ((k & 3) << 2);
+      b_off0 = (uint32_t)(((int64_t)k * p.ldb + n0 + cc * 8) * 2);
+    }
   }
-  // byte stride of instruction i within the stage (wave-uniform)
-  auto a_istride = [&](int i) -> uint32_t {
+  __device__ __forceinline__ uint32_t a_istride(int i) const {
     if constexpr (!AMN) return (uint32_t)((int64_t)i * NW * RPI * p.lda * 2);
     else return (uint32_t)((int64_t)i * (64 * NW / (BM / 8)) * p.lda * 2);
-  };
-  auto b_istride = [&](int i) -> uint32_t {
+  }
+  __device__ __forceinline__ uint32_t b_istride(int i) const {
     if constexpr (!BMN) {
       int64_t row = (int64_t)i * NW * RPI;
       if (Tr::split && row >= BN / 2) row += p.I - BN / 2;   // up rows follow the gate rows
@@ -931,33 +949,37 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
     } else {
       return (uint32_t)((int64_t)i * (64 * NW / (BN / 8)) * p.ldb * 2);
     }
-  };
-  const uint32_t a_kstep = AMN ? (uint32_t)(BK * p.lda * 2) : (uint32_t)(BK * 2);
-  const uint32_t b_kstep = BMN ? (uint32_t)(BK * p.ldb * 2) : (uint32_t)(BK * 2);
-  // DMA instruction d (0..L-1) of stage kt into slot
-  auto dma_one = [&](int d, int kt, int slot) {
+  }
+  // DMA instruction d (0..L-1) of stage kt into slot.
+  __device__ __forceinline__ void dma_one(int d, int kt, int slot) {
     const uint32_t sl = lds_base + slot * STAGE;
     if (d < LA) {
       dma16(ra, a_off0 + uniform(kt * a_kstep + a_istride(d)), sl + (d * NW + wave) * 1024);
     } else {
       const int i = d - LA;
-      dma16(rb, b_off0 + uniform(kt * b_kstep + b_istride(i)), sl + A_BYTES + (i * NW + wave) * 1024);
+      dma16(rb, b_off0 + uniform(kt * b_kstep + b_istride(i)),
+            sl + A_BYTES + (i * NW + wave) * 1024);
     }
-  };
+  }
+  __device__ __forceinline__ void issue_stage(int kt, int slot) {
+#pragma unroll
+    for (int d = 0; d < L; ++d) dma_one(d, kt, slot);
+  }
 
-  // ---- fragments -----------------------------------------------------------------------------------
-  auto b_row = [&](int j) {
+  // ---- fragments ----------------------------------------------------------------------------------
+  __device__ __forceinline__ int b_row(int j) const {
     if (Tr::split) return (j / (TN / 2)) * (BN / 2) + wn * (WTN / 2) + (j % (TN / 2)) * 32;
     return wn * WTN + j * 32;
-  };
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int grp = lane >> 4, li = lane & 15;
-  auto frag_k = [&](int base, int row0, int kk) -> bf16x8_t {
-    const int r = row0 + l32;
+  }
+  __device__ __forceinline__ bf16x8_t frag_k(int base, int row0, int kk) const {
+    const int r = row0 + (lane & 31);
     return *reinterpret_cast<const bf16x8_t*>(smem + base + r * (BK * 2) +
-                                              kswz<BK>(r, 2 * kk + hi) * 16);
-  };
-  auto frag_t = [&](int base, int rows, int col0, int kk) -> bf16x8_t {
+                                              kswz<BK>(r, 2 * kk + (lane >> 5)) * 16);
+  }
+  // MN-major: two transposed 8-byte reads give columns col0 + (grp&1)*16 + li,
+  // k = kk*16 + (grp>>1)*8 + 0..7.
+  __device__ __forceinline__ bf16x8_t frag_t(int base, int rows, int col0, int kk) const {
+    const int grp = lane >> 4, li = lane & 15;
     const int col = col0 + (grp & 1) * 16 + 4 * (li & 3);
     const int cc = col >> 3, half = ((col >> 2) & 1) * 8;
     const int k0 = kk * 16 + (grp >> 1) * 8 + (li >> 2);
@@ -970,9 +992,8 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
     __builtin_memcpy(&r, &lo, 8);
     __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi2, 8);
     return r;
-  };
-  struct Frags { bf16x8_t a[TM], b[TN]; };
-  auto load = [&](int slot, int kk, Frags& f) {
+  }
+  __device__ __forceinline__ void load(int slot, int kk, Frags& f) const {
     const int sa = slot * STAGE, sb = sa + A_BYTES;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -984,19 +1005,12 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
       if constexpr (BMN) f.b[j] = frag_t(sb, BN, b_row(j), kk);
       else f.b[j] = frag_k(sb, b_row(j), kk);
     }
-  };
-
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  }
   // The slice's MFMAs with DMA instructions [D0, D1) of stage kt_dma spread evenly among them.
-  auto mma_dma = [&](const Frags& f, auto d0c, auto d1c, bool on, int kt_dma, int slot_dma) {
-    constexpr int D0 = decltype(d0c)::value, D1 = decltype(d1c)::value, N = D1 - D0;
-    constexpr int T = TM * TN;
+  template <int D0, int D1>
+  __device__ __forceinline__ void mma_dma(Acc& acc, const Frags& f, bool on, int kt_dma,
+                                          int slot_dma) {
+    constexpr int N = D1 - D0, T = TM * TN;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       acc[t / TN][t % TN] = Mf::run(f.b[t % TN], f.a[t / TN], acc[t / TN][t % TN]);
@@ -1010,52 +1024,77 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
           }
       }
     }
-  };
-  typedef std::integral_constant<int, 0> C0;
-  typedef std::integral_constant<int, TL::P1> CP1;
-  typedef std::integral_constant<int, TL::P2> CP2;
-  typedef std::integral_constant<int, L> CL;
+  }
+  __device__ __forceinline__ static void zero(Acc& acc) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  }
 
-  // ---- main loop: stage kt in slot kt & 1 ---------------------------------------------------------
-  const int nk = (klen + BK - 1) / BK;
-  if (nk > 0) {
-#pragma unroll
-    for (int d = 0; d < L; ++d) dma_one(d, 0, 0);
-    if (nk > 1) {
-#pragma unroll
-      for (int d = 0; d < L; ++d) dma_one(d, 1, 1);
-      wait_vm<L>();
-    } else {
-      wait_vm<0>();
-    }
-    block_barrier();
+  // Contraction of a tile of nk >= 1 stages whose stages 0 and 1 are issued and whose stage 0 is
+  // visible to every wavefront (stage kt lives in slot kt & 1). S > 0 with stores_pending: this
+  // wave issued S stores after stage 1 (a previous tile's epilogue) that need not wait for it.
+  // at_end() runs once, in the last stage, after this wave's last fragment reads are issued and
+  // before the last slice's MFMAs.
+  template <int S, class AtEnd>
+  __device__ __forceinline__ void run(Acc& acc, int nk, bool stores_pending, AtEnd at_end) {
     for (int kt = 0; kt < nk; ++kt) {
       const int slot = kt & 1;
       const bool pend = kt >= 1 && kt + 1 < nk;   // stage kt + 1 still has DMA to issue
       const bool refill = kt + 2 < nk;            // stage kt + 2 goes into this slot
       Frags f;
       load(slot, 0, f);
-      mma_dma(f, CP1(), CP2(), pend, kt + 1, slot ^ 1);
+      mma_dma<TL::P1, TL::P2>(acc, f, pend, kt + 1, slot ^ 1);
       load(slot, 1, f);
-      mma_dma(f, CP2(), CL(), pend, kt + 1, slot ^ 1);
+      mma_dma<TL::P2, L>(acc, f, pend, kt + 1, slot ^ 1);
       load(slot, 2, f);
-      mma_dma(f, C0(), C0(), false, 0, 0);
+      mma_dma<0, 0>(acc, f, false, 0, 0);
       load(slot, 3, f);
       if (kt + 1 < nk) {
         // This wave's DMA of stage kt + 1 has landed and its reads of this slot are done; the
         // barrier makes both true for every wave, so stage kt + 1 is visible and the slot free.
-        wait_vm<0>();
+        if (S > 0 && kt == 0 && stores_pending) wait_vm<S>();
+        else wait_vm<0>();
         wait_lgkm0();
         block_barrier();
+      } else {
+        at_end();
       }
-      mma_dma(f, C0(), CP1(), refill, kt + 2, slot);
+      mma_dma<0, TL::P1>(acc, f, refill, kt + 2, slot);
     }
   }
+};
+
+// One tile on the eight-wavefront engine, epilogue through the freed ring.
+template <int KIND, class TL>
+__device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* smem, int g, int m0,
+                                           int n0, int kbeg, int klen) {
+  typedef Eng8<KIND, TL> E;
+  E e(p, smem);
+  e.setup(g, m0, n0, kbeg, klen);
+  typename E::Acc acc;
+  E::zero(acc);
+  const int nk = (klen + TL::BK - 1) / TL::BK;
+  if (nk > 0) {
+    e.issue_stage(0, 0);
+    if (nk > 1) {
+      e.issue_stage(1, 1);
+      wait_vm<TL::L>();
+    } else {
+      wait_vm<0>();
+    }
+    block_barrier();
+    e.template run<0>(acc, nk, false, [] {});
+  }
   // Every wavefront is done with the ring: the two stages become per-wavefront staging buffers.
-  static_assert(2 * STAGE / NW >= 8192, "8 KiB of LDS per wavefront for the epilogue");
+  static_assert(2 * TL::STAGE / TL::NW >= 8192, "8 KiB of LDS per wavefront for the epilogue");
   wait_lgkm0();
   block_barrier();
-  store_tile8<KIND, TM, TN, WTM, WTN>(p, acc, g, m0, n0, wm, wn, lane, smem + wave * (2 * STAGE / NW));
+  store_tile8<KIND, TL::TM, TL::TN, TL::WTM, TL::WTN>(p, acc, g, m0, n0, e.wm, e.wn, e.lane,
+                                                      smem + e.wave * (2 * TL::STAGE / TL::NW));
 }
 
 // Tall tiles on the eight-wavefront engine: 4 x 2 wavefronts over 256 columns (128 for the
@@ -1178,20 +1217,125 @@ __global__ __launch_bounds__(kThreads, 1) void ggemm_block64_kernel(GemmArgs p) 
   pipe_tile<KIND, Block64Tile>(p, smem, g, m0, n0, 0, p.K);
 }
 
-// Weight-gradient kinds on the eight-wavefront engine: 256 weight rows x 256 columns per tile,
-// contraction over the segment's rows (both operands MN-major in HBM).
+// Weight-gradient kinds: 256 weight rows x 256 columns per tile, contraction over the segment's
+// rows (both operands MN-major in HBM). The contraction is short (one segment), so a tile's
+// fixed costs (first DMA, 128 KiB of stores) are as large as its MFMAs: the kernel is persistent,
+// one workgroup per CU walking its XCD's tiles, and it issues the next tile's first two stages
+// before storing the current tile, so the stores drain under the next tile's MFMAs.
 typedef Tile8<256, 256, 4, 2> Wgrad8Tile;
+constexpr int kWgradScr = 4096;                     // epilogue staging per wavefront
+constexpr int kWgradStores = Wgrad8Tile::TM * (Wgrad8Tile::TN / 2) * 4;   // stores per wave per tile
+static_assert(2 * Wgrad8Tile::STAGE + Wgrad8Tile::NW * kWgradScr <= kLdsBytes, "LDS budget");
+static_assert(Wgrad8Tile::L + kWgradStores < 64, "vmcnt range");
+
+// Epilogue with 32 x 64 staging passes and bounds-checked buffer stores: lanes outside the
+// weight matrix get an offset past the buffer's end, which the hardware drops, so every
+// wavefront issues exactly kWgradStores stores per tile (the kernel's vmcnt waits count them).
+template <int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void store_wgrad8(const GemmArgs& p, const f32x16_t (&acc)[TM][TN],
+                                             int g, int m0, int n0, int wm, int wn, int lane,
+                                             unsigned char* scr) {
+  static_assert(TM * (TN / 2) * 4 == kWgradStores, "store count");
+  uint16_t* out = p.out + (int64_t)g * p.o_gstride;
+  const uint32_t bytes = (uint32_t)((int64_t)p.M * p.ldo * 2);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(out, 0, (int)bytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int h = 0; h < TN / 2; ++h) {
+      const int mrow = m0 + wm * WTM + i * 32, c0 = n0 + wn * WTN + h * 64;
+      stage_bf16<2>(scr, lane, [&](int j, int q, int e) { return acc[i][2 * h + j][4 * q + e]; },
+          [&](int rr, int c, uint4 d) {
+            const int m = mrow + rr, col = c0 + c;
+            const uint32_t off =
+                (m < p.M && col < p.N) ? (uint32_t)(((int64_t)m * p.ldo + col) * 2) : 0x80000000u;
+            typedef uint32_t v4_t __attribute__((ext_vector_type(4)));
+            const v4_t v = {d.x, d.y, d.z, d.w};
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+          });
+    }
+}
+
+// A wave-uniform read of a read-only int array through the scalar data cache (the constant
+// address space), so it does not join the vector-memory queue that the DMA waits count.
+__device__ __forceinline__ int ld_scalar(const int32_t* a, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)a)[i];
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * Wgrad8Tile::STAGE];
-  const int64_t per_g = (int64_t)p.n_tiles_m * p.n_tiles_n;
-  const int64_t L = xcd_remap(blockIdx.x, per_g * p.G);
-  if (L < 0) return;
-  const int g = (int)(L / per_g);
-  const int rem = (int)(L % per_g);
-  const int m0 = (rem / p.n_tiles_n) * Wgrad8Tile::BM, n0 = (rem % p.n_tiles_n) * Wgrad8Tile::BN;
-  const int kbeg = p.seg[g], klen = p.seg[g + 1] - kbeg;
-  pipe8_tile<KIND, Wgrad8Tile>(p, smem, g, m0, n0, kbeg, klen);
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
+  typedef Wgrad8Tile TL;
+  typedef Eng8<KIND, TL> E;
+  constexpr int S = kWgradStores, L = TL::L;
+  const int64_t per_g = (int64_t)p.n_tiles_m * p.n_tiles_n, total = per_g * p.G;
+  const int64_t per_x = (total + kNumXcd - 1) / kNumXcd;   // each XCD walks a contiguous range
+  const int xcd = blockIdx.x % kNumXcd, nwg = gridDim.x / kNumXcd;
+  const int64_t lend = min((int64_t)(xcd + 1) * per_x, total);
+  int64_t l = (int64_t)xcd * per_x + blockIdx.x / kNumXcd;
+  if (l >= lend) return;
+  struct T { int g, m0, n0, kbeg, klen, nk; };
+  auto decode = [&](int64_t L0) {
+    T t;
+    t.g = (int)(L0 / per_g);
+    const int rem = (int)(L0 % per_g);
+    t.m0 = (rem / p.n_tiles_n) * TL::BM;
+    t.n0 = (rem % p.n_tiles_n) * TL::BN;
+    t.kbeg = ld_scalar(p.seg, t.g);
+    t.klen = ld_scalar(p.seg, t.g + 1) - t.kbeg;
+    t.nk = (t.klen + TL::BK - 1) / TL::BK;
+    return t;
+  };
+  E e(p, smem);
+  unsigned char* scr = smem + 2 * TL::STAGE + e.wave * kWgradScr;
+  T cur = decode(l);
+  e.setup(cur.g, cur.m0, cur.n0, cur.kbeg, cur.klen);
+  if (cur.nk > 0) e.issue_stage(0, 0);
+  if (cur.nk > 1) e.issue_stage(1, 1);
+  bool stores = false;   // this wave's previous-tile stores are queued after the first two stages
+  for (;;) {
+    if (cur.nk > 0) {
+      // stage 0 of this tile has landed (stage 1 and the previous tile's stores may still be out)
+      if (cur.nk > 1) {
+        if (stores) wait_vm<L + S>(); else wait_vm<L>();
+      } else {
+        if (stores) wait_vm<S>(); else wait_vm<0>();
+      }
+    }
+    block_barrier();
+    typename E::Acc acc;
+    E::zero(acc);
+    const int64_t ln = l + nwg;
+    const bool has_next = ln < lend;
+    T nxt = cur;
+    if (has_next) nxt = decode(ln);
+    // Once every wave is done with the ring, start the next tile's first two stages.
+    auto at_end = [&] {
+      wait_lgkm0();
+      block_barrier();
+      if (has_next) {
+        e.setup(nxt.g, nxt.m0, nxt.n0, nxt.kbeg, nxt.klen);
+        if (nxt.nk > 0) e.issue_stage(0, 0);
+        if (nxt.nk > 1) e.issue_stage(1, 1);
+      }
+    };
+    if (cur.nk > 0) e.template run<S>(acc, cur.nk, stores, at_end);
+    else at_end();
+    store_wgrad8<TL::TM, TL::TN, TL::WTM, TL::WTN>(p, acc, cur.g, cur.m0, cur.n0, e.wm, e.wn,
+                                                   e.lane, scr);
+    if (!has_next) break;
+    l = ln;
+    cur = nxt;
+    stores = true;
+  }
+}
+
+// Workgroups of a persistent launch: one per CU of MI355X (8 XCDs x 32 CUs), fewer for small
+// problems; a multiple of the XCD count so every XCD gets the same number.
+constexpr int kPersistentWgs = kNumXcd * 32;
+unsigned persistent_grid(int64_t tiles) {
+  const int64_t per_xcd = (tiles + kNumXcd - 1) / kNumXcd;
+  return (unsigned)(kNumXcd * (per_xcd < kPersistentWgs / kNumXcd ? per_xcd : kPersistentWgs / kNumXcd));
 }
 
 template <int KIND, int BM, int BN, int MS, int WAVES_M>
@@ -1313,9 +1457,8 @@ hipError_t launch_ggemm_wgrad(const moe_shape_t& s, uint32_t which, const uint16
   g.n_tiles_n = (g.N + Wgrad8Tile::BN - 1) / Wgrad8Tile::BN;
   int64_t tiles = (int64_t)g.G * g.n_tiles_m * g.n_tiles_n;
   if (which & MOE_WGRAD_DOWN) {
-    hipLaunchKernelGGL((ggemm_wgrad8_kernel<kWgradDown>),
-                       dim3((unsigned)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd)), dim3(kThreads8),
-                       0, st, g);
+    hipLaunchKernelGGL((ggemm_wgrad8_kernel<kWgradDown>), dim3(persistent_grid(tiles)),
+                       dim3(kThreads8), 0, st, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1328,9 +1471,8 @@ hipError_t launch_ggemm_wgrad(const moe_shape_t& s, uint32_t which, const uint16
   g.n_tiles_m = (g.M + Wgrad8Tile::BM - 1) / Wgrad8Tile::BM;
   g.n_tiles_n = (g.N + Wgrad8Tile::BN - 1) / Wgrad8Tile::BN;
   tiles = (int64_t)g.G * g.n_tiles_m * g.n_tiles_n;
-  hipLaunchKernelGGL((ggemm_wgrad8_kernel<kWgradGateUp>),
-                     dim3((unsigned)((tiles + kNumXcd - 1) / kNumXcd * kNumXcd)), dim3(kThreads8), 0,
-                     st, g);
+  hipLaunchKernelGGL((ggemm_wgrad8_kernel<kWgradGateUp>), dim3(persistent_grid(tiles)),
+                     dim3(kThreads8), 0, st, g);
   return hipGetLastError();
 }
 
