@@ -199,6 +199,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": dom,
+                "traffic_gbs": (round(traffic / (stage_ms[dom] * 1e-3) / 1e9, 1)
+                                if traffic is not None else None),
                 "per_unit": f"{per_row[dom]:.0f} FLOP per routed row x {rows} rows per launch",
                 "avg_launch_ms": round(stage_ms[dom], 4)}
     out = {

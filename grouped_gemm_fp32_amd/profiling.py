@@ -24,9 +24,12 @@ import sys
 
 # rocprofv3 kernel name -> the stage names bench.py reports
 STAGE_OF = {
-    "ggemm_tall_kernel<0>": "fwd_gateup", "ggemm_tall_kernel<1>": "fwd_down",
-    "ggemm_tall_kernel<2>": "dgrad_down", "ggemm_tall_kernel<3>": "dgrad_gateup",
-    "ggemm_wgrad_kernel<4>": "wgrad_down", "ggemm_wgrad_kernel<5>": "wgrad_gateup",
+    "ggemm_tall8_kernel<0>": "fwd_gateup", "ggemm_tall8_kernel<1>": "fwd_down",
+    "ggemm_tall8_kernel<2>": "dgrad_down", "ggemm_tall8_kernel<3>": "dgrad_gateup",
+    "ggemm_wgrad8_kernel<4>": "wgrad_down", "ggemm_wgrad8_kernel<5>": "wgrad_gateup",
+    "gather_rows_kernel": "permute", "gather_sum_kernel<true>": "combine",
+    "combine_bwd_kernel": "combine_bwd", "gather_sum_kernel<false>": "unpermute_bwd",
+    "route_kernel<1>": "route",
 }
 
 
