@@ -814,9 +814,13 @@ __device__ __forceinline__ void store_tile8(const GemmArgs& p, const f32x16_t (&
       }
     } else if constexpr (KIND == kDgradDown) {
       // da (fp32) meets the saved h: dg = da*u*s*(1 + g*(1 - s)), du = da*g*s, s = sigmoid(g).
-      const int c0 = n0 + wn * WTN;
+      // in passes of 64 columns, which keeps the epilogue's registers within budget
+      static_assert(TN % 2 == 0, "64-column passes");
+#pragma unroll
+      for (int h = 0; h < TN / 2; ++h) {
+      const int c0 = n0 + wn * WTN + h * 64;
       const int64_t ldh = 2 * (int64_t)p.I;
-      stage_f32<TN>(scr, lane, [&](int j, int q, int e) { return acc[i][j][4 * q + e]; },
+      stage_f32<2>(scr, lane, [&](int j, int q, int e) { return acc[i][2 * h + j][4 * q + e]; },
           [&](int rr, int c, float4 da) {
             if (c0 + c >= p.N) return;
             const int64_t hrow = (mrow + rr) * ldh + c0 + c;
@@ -836,6 +840,7 @@ __device__ __forceinline__ void store_tile8(const GemmArgs& p, const f32x16_t (&
             *reinterpret_cast<uint2*>(p.out + hrow + p.I) =
                 make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
           });
+      }
     } else {
       uint16_t* out = p.out + (Tr::grouped_rows ? 0 : (int64_t)g * p.o_gstride);
       const int c0 = n0 + wn * WTN;
@@ -895,10 +900,13 @@ struct Eng8 {
   lds_u8_t* s3;
   uint32_t lds_base;
   int lane, wave, wm, wn;
-  // DMA state of the tile being loaded: one lane offset per operand, instruction i adds a
-  // wave-uniform stride, stage kt adds kt * kstep.
-  v4u32_t ra, rb;
-  uint32_t a_off0, b_off0, a_kstep, b_kstep;
+  // DMA state of one tile: buffer resources and one lane offset per operand; instruction i adds
+  // a wave-uniform stride, stage kt adds kt * kstep.
+  struct Dma {
+    v4u32_t ra, rb;
+    uint32_t a_off0, b_off0;
+  };
+  uint32_t a_kstep, b_kstep;
 
   __device__ __forceinline__ Eng8(const GemmArgs& p_, unsigned char* smem_) : p(p_), smem(smem_) {
     s3 = (lds_u8_t*)smem;
@@ -913,28 +921,28 @@ struct Eng8 {
 
   // Tile: rows m0.. of group g (row-grouped kinds) or weight rows m0.. of group g (wgrad),
   // columns n0.., contraction over [kbeg, kbeg + klen).
-  __device__ __forceinline__ void setup(int g, int m0, int n0, int kbeg, int klen) {
-    if (AMN) ra = make_rsrc(p.a + (int64_t)kbeg * p.lda, (int64_t)klen * p.lda * 2);
-    else ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)BM * p.lda * 2);
-    if (Tr::grouped_rows) rb = make_rsrc(p.b + (int64_t)g * p.b_gstride, p.b_gstride * 2);
-    else rb = make_rsrc(p.b + (int64_t)kbeg * p.ldb, (int64_t)klen * p.ldb * 2);
+  __device__ __forceinline__ void setup(Dma& st, int g, int m0, int n0, int kbeg, int klen) const {
+    if (AMN) st.ra = make_rsrc(p.a + (int64_t)kbeg * p.lda, (int64_t)klen * p.lda * 2);
+    else st.ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)BM * p.lda * 2);
+    if (Tr::grouped_rows) st.rb = make_rsrc(p.b + (int64_t)g * p.b_gstride, p.b_gstride * 2);
+    else st.rb = make_rsrc(p.b + (int64_t)kbeg * p.ldb, (int64_t)klen * p.ldb * 2);
     if constexpr (!AMN) {
       const int r = wave * RPI + lane / CPR;
-      a_off0 = (uint32_t)(((int64_t)r * p.lda + kswz<BK>(r, lane % CPR) * 8) * 2);
+      st.a_off0 = (uint32_t)(((int64_t)r * p.lda + kswz<BK>(r, lane % CPR) * 8) * 2);
     } else {
       constexpr int CPRM = BM / 8;
       static_assert((64 * NW) % (4 * CPRM) == 0, "instruction stride must keep k & 3");
       const int f = wave * 64 + lane, k = f / CPRM, cc = (f % CPRM) ^ ((k & 3) << 2);
-      a_off0 = (uint32_t)(((int64_t)k * p.lda + m0 + cc * 8) * 2);
+      st.a_off0 = (uint32_t)(((int64_t)k * p.lda + m0 + cc * 8) * 2);
     }
     if constexpr (!BMN) {
       const int r = wave * RPI + lane / CPR;
-      b_off0 = (uint32_t)(((int64_t)(n0 + r) * p.ldb + kswz<BK>(r, lane % CPR) * 8) * 2);
+      st.b_off0 = (uint32_t)(((int64_t)(n0 + r) * p.ldb + kswz<BK>(r, lane % CPR) * 8) * 2);
     } else {
       constexpr int CPRM = BN / 8;
       static_assert((64 * NW) % (4 * CPRM) == 0, "instruction stride must keep k & 3");
       const int f = wave * 64 + lane, k = f / CPRM, cc = (f % CPRM) ^ ((k & 3) << 2);
-      b_off0 = (uint32_t)(((int64_t)k * p.ldb + n0 + cc * 8) * 2);
+      st.b_off0 = (uint32_t)(((int64_t)k * p.ldb + n0 + cc * 8) * 2);
     }
   }
   __device__ __forceinline__ uint32_t a_istride(int i) const {
@@ -950,20 +958,20 @@ struct Eng8 {
       return (uint32_t)((int64_t)i * (64 * NW / (BN / 8)) * p.ldb * 2);
     }
   }
-  // DMA instruction d (0..L-1) of stage kt into slot.
-  __device__ __forceinline__ void dma_one(int d, int kt, int slot) {
+  // DMA instruction d (0..L-1) of stage kt of tile st into slot.
+  __device__ __forceinline__ void dma_one(const Dma& st, int d, int kt, int slot) const {
     const uint32_t sl = lds_base + slot * STAGE;
     if (d < LA) {
-      dma16(ra, a_off0 + uniform(kt * a_kstep + a_istride(d)), sl + (d * NW + wave) * 1024);
+      dma16(st.ra, st.a_off0 + uniform(kt * a_kstep + a_istride(d)), sl + (d * NW + wave) * 1024);
     } else {
       const int i = d - LA;
-      dma16(rb, b_off0 + uniform(kt * b_kstep + b_istride(i)),
+      dma16(st.rb, st.b_off0 + uniform(kt * b_kstep + b_istride(i)),
             sl + A_BYTES + (i * NW + wave) * 1024);
     }
   }
-  __device__ __forceinline__ void issue_stage(int kt, int slot) {
+  __device__ __forceinline__ void issue_stage(const Dma& st, int kt, int slot) const {
 #pragma unroll
-    for (int d = 0; d < L; ++d) dma_one(d, kt, slot);
+    for (int d = 0; d < L; ++d) dma_one(st, d, kt, slot);
   }
 
   // ---- fragments ----------------------------------------------------------------------------------
@@ -1006,10 +1014,12 @@ struct Eng8 {
       else f.b[j] = frag_k(sb, b_row(j), kk);
     }
   }
-  // The slice's MFMAs with DMA instructions [D0, D1) of stage kt_dma spread evenly among them.
+  // The slice's MFMAs with DMA instructions [D0, D1) of stage kt_dma of tile st spread evenly
+  // among them.
+  // With nd < D1 - D0 only the first nd of them are issued.
   template <int D0, int D1>
-  __device__ __forceinline__ void mma_dma(Acc& acc, const Frags& f, bool on, int kt_dma,
-                                          int slot_dma) {
+  __device__ __forceinline__ void mma_dma(Acc& acc, const Frags& f, bool on, const Dma& st,
+                                          int kt_dma, int slot_dma, int nd = D1 - D0) const {
     constexpr int N = D1 - D0, T = TM * TN;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -1017,9 +1027,9 @@ struct Eng8 {
       if constexpr (N > 0) {
 #pragma unroll
         for (int d = 0; d < N; ++d)
-          if (t == (d + 1) * T / (N + 1) - 1 && on) {
+          if (t == d * T / N && on && d < nd) {   // d*T/N is in [0, T) for any N
             __builtin_amdgcn_sched_barrier(0);
-            dma_one(D0 + d, kt_dma, slot_dma);
+            dma_one(st, D0 + d, kt_dma, slot_dma);
             __builtin_amdgcn_sched_barrier(0);
           }
       }
@@ -1034,36 +1044,54 @@ struct Eng8 {
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
   }
 
-  // Contraction of a tile of nk >= 1 stages whose stages 0 and 1 are issued and whose stage 0 is
-  // visible to every wavefront (stage kt lives in slot kt & 1). S > 0 with stores_pending: this
-  // wave issued S stores after stage 1 (a previous tile's epilogue) that need not wait for it.
-  // at_end() runs once, in the last stage, after this wave's last fragment reads are issued and
-  // before the last slice's MFMAs.
-  template <int S, class AtEnd>
-  __device__ __forceinline__ void run(Acc& acc, int nk, bool stores_pending, AtEnd at_end) {
+  // Contraction of a tile of nk >= 1 stages, stage kt in slot (s0 + kt) & 1. On entry stage 0
+  // is visible to every wavefront and stage 1 (if any) is fully issued. S > 0 with
+  // stores_pending: this wave issued S stores after stage 1 (a previous tile's epilogue) that
+  // need not wait for it.
+  // With `chain` (this tile and the next both have at least two stages) the DMA runs on into the
+  // next tile nx: its stage 0 is issued like any other stage during this tile's last two stages
+  // and its stage 1 in full during the last slice, so on return the next tile meets the entry
+  // condition above with s0' = (s0 + nk) & 1. Without it, at_end() runs once in the last stage,
+  // after this wave's last fragment reads are issued and before the last slice's MFMAs.
+  template <int S, bool CHAIN, class AtEnd>
+  __device__ __forceinline__ void run(Acc& acc, const Dma& cu, int nk, int s0, bool stores_pending,
+                                      const Dma& nx, bool chain_, AtEnd at_end) {
+    const bool chain = CHAIN && chain_;
     for (int kt = 0; kt < nk; ++kt) {
-      const int slot = kt & 1;
-      const bool pend = kt >= 1 && kt + 1 < nk;   // stage kt + 1 still has DMA to issue
-      const bool refill = kt + 2 < nk;            // stage kt + 2 goes into this slot
+      const int slot = (s0 + kt) & 1;
+      // stage kt + 1: this tile's or (chain) the next tile's stage 0; its first DMA part was
+      // issued in the previous stage unless it is this tile's stage 1
+      const bool nx1 = CHAIN && kt + 1 >= nk;
+      const bool pend = kt >= 1 && (kt + 1 < nk || chain);
+      const Dma& st1 = nx1 ? nx : cu;
+      const int k1 = nx1 ? 0 : kt + 1;
       Frags f;
       load(slot, 0, f);
-      mma_dma<TL::P1, TL::P2>(acc, f, pend, kt + 1, slot ^ 1);
+      mma_dma<TL::P1, TL::P2>(acc, f, pend, st1, k1, slot ^ 1);
       load(slot, 1, f);
-      mma_dma<TL::P2, L>(acc, f, pend, kt + 1, slot ^ 1);
+      mma_dma<TL::P2, L>(acc, f, pend, st1, k1, slot ^ 1);
       load(slot, 2, f);
-      mma_dma<0, 0>(acc, f, false, 0, 0);
+      mma_dma<0, 0>(acc, f, false, cu, 0, 0);
       load(slot, 3, f);
-      if (kt + 1 < nk) {
+      if (kt + 1 < nk || chain) {
         // This wave's DMA of stage kt + 1 has landed and its reads of this slot are done; the
         // barrier makes both true for every wave, so stage kt + 1 is visible and the slot free.
         if (S > 0 && kt == 0 && stores_pending) wait_vm<S>();
         else wait_vm<0>();
         wait_lgkm0();
         block_barrier();
-      } else {
-        at_end();
       }
-      mma_dma<0, TL::P1>(acc, f, refill, kt + 2, slot);
+      if constexpr (!CHAIN) {
+        if (kt + 1 == nk) at_end();
+        mma_dma<0, TL::P1>(acc, f, kt + 2 < nk, cu, kt + 2, slot);   // this tile's stage kt + 2
+      } else {
+        // stage kt + 2 of the stream: this tile's (first part), the next tile's stage 0 (first
+        // part) or the next tile's stage 1 (whole, since that tile starts with it issued)
+        if (kt + 1 == nk && !chain) at_end();
+        const bool own = kt + 2 < nk;
+        mma_dma<0, L>(acc, f, own || chain, own ? cu : nx, own ? kt + 2 : kt + 2 - nk, slot,
+                      kt + 2 <= nk ? TL::P1 : L);
+      }
     }
   }
 };
@@ -1074,20 +1102,21 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
                                            int n0, int kbeg, int klen) {
   typedef Eng8<KIND, TL> E;
   E e(p, smem);
-  e.setup(g, m0, n0, kbeg, klen);
+  typename E::Dma st;
+  e.setup(st, g, m0, n0, kbeg, klen);
   typename E::Acc acc;
   E::zero(acc);
   const int nk = (klen + TL::BK - 1) / TL::BK;
   if (nk > 0) {
-    e.issue_stage(0, 0);
+    e.issue_stage(st, 0, 0);
     if (nk > 1) {
-      e.issue_stage(1, 1);
+      e.issue_stage(st, 1, 1);
       wait_vm<TL::L>();
     } else {
       wait_vm<0>();
     }
     block_barrier();
-    e.template run<0>(acc, nk, false, [] {});
+    e.template run<0, false>(acc, st, nk, 0, false, st, false, [] {});
   }
   // Every wavefront is done with the ring: the two stages become per-wavefront staging buffers.
   static_assert(2 * TL::STAGE / TL::NW >= 8192, "8 KiB of LDS per wavefront for the epilogue");
@@ -1097,11 +1126,10 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
                                                       smem + e.wave * (2 * TL::STAGE / TL::NW));
 }
 
-// Tall tiles on the eight-wavefront engine: 4 x 2 wavefronts over 256 columns (128 for the
-// dgrad of the down projection, whose SwiGLU-backward epilogue needs the registers and whose
-// I columns are a multiple of 128 but not of 256).
-template <int KIND> constexpr int tall8_bn() { return KIND == kDgradDown ? 128 : 256; }
-template <int KIND, int ROWS> struct Tall8 { typedef Tile8<ROWS, tall8_bn<KIND>(), 4, 2> type; };
+// Tall tiles on the eight-wavefront engine: 4 x 2 wavefronts over 256 columns (a ragged last
+// column tile, e.g. I = 1408 for the dgrad of the down projection, is cut by the epilogue).
+constexpr int kTall8BN = 256;
+template <int ROWS> struct Tall8 { typedef Tile8<ROWS, kTall8BN, 4, 2> type; };
 
 template <int KIND>
 __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
@@ -1146,10 +1174,10 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   const int local = ti - t0, base = nb / ntg, extra = nb % ntg;
   const int blk0 = local * base + min(local, extra), nblk = base + (local < extra ? 1 : 0);
   const int m0 = p.seg[g] + blk0 * kTallBlk;
-  const int n0 = nt * tile_cols<KIND>(tall8_bn<KIND>());
-  if (nblk == 3) pipe8_tile<KIND, typename Tall8<KIND, 384>::type>(p, smem, g, m0, n0, 0, p.K);
-  else if (nblk == 2) pipe8_tile<KIND, typename Tall8<KIND, 256>::type>(p, smem, g, m0, n0, 0, p.K);
-  else pipe8_tile<KIND, typename Tall8<KIND, 128>::type>(p, smem, g, m0, n0, 0, p.K);
+  const int n0 = nt * tile_cols<KIND>(kTall8BN);
+  if (nblk == 3) pipe8_tile<KIND, Tall8<384>::type>(p, smem, g, m0, n0, 0, p.K);
+  else if (nblk == 2) pipe8_tile<KIND, Tall8<256>::type>(p, smem, g, m0, n0, 0, p.K);
+  else pipe8_tile<KIND, Tall8<128>::type>(p, smem, g, m0, n0, 0, p.K);
 }
 
 // Row-grouped kinds with block_m a multiple of 128: every segment is cut into ceil(blocks / 3)
@@ -1288,44 +1316,56 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) 
   };
   E e(p, smem);
   unsigned char* scr = smem + 2 * TL::STAGE + e.wave * kWgradScr;
+  typename E::Dma dc, dn;   // DMA state of the current and the next tile
   T cur = decode(l);
-  e.setup(cur.g, cur.m0, cur.n0, cur.kbeg, cur.klen);
-  if (cur.nk > 0) e.issue_stage(0, 0);
-  if (cur.nk > 1) e.issue_stage(1, 1);
-  bool stores = false;   // this wave's previous-tile stores are queued after the first two stages
+  e.setup(dc, cur.g, cur.m0, cur.n0, cur.kbeg, cur.klen);
+  if (cur.nk > 0) e.issue_stage(dc, 0, 0);
+  if (cur.nk > 1) e.issue_stage(dc, 1, 1);
+  int s0 = 0;             // slot of the current tile's stage 0
+  bool stores = false;    // this wave's previous-tile stores are queued after the first two stages
+  bool ready = false;     // the current tile's stage 0 is already visible (chained DMA)
   for (;;) {
-    if (cur.nk > 0) {
-      // stage 0 of this tile has landed (stage 1 and the previous tile's stores may still be out)
-      if (cur.nk > 1) {
-        if (stores) wait_vm<L + S>(); else wait_vm<L>();
-      } else {
-        if (stores) wait_vm<S>(); else wait_vm<0>();
+    if (!ready) {
+      if (cur.nk > 0) {
+        // stage 0 of this tile has landed (stage 1 and the previous tile's stores may be out)
+        if (cur.nk > 1) {
+          if (stores) wait_vm<L + S>(); else wait_vm<L>();
+        } else {
+          if (stores) wait_vm<S>(); else wait_vm<0>();
+        }
       }
+      block_barrier();
     }
-    block_barrier();
     typename E::Acc acc;
     E::zero(acc);
     const int64_t ln = l + nwg;
     const bool has_next = ln < lend;
     T nxt = cur;
-    if (has_next) nxt = decode(ln);
-    // Once every wave is done with the ring, start the next tile's first two stages.
+    if (has_next) {
+      nxt = decode(ln);
+      e.setup(dn, nxt.g, nxt.m0, nxt.n0, nxt.kbeg, nxt.klen);
+    }
+    // The next tile's first stages follow this tile's in the same DMA stream when both have at
+    // least two; otherwise they are issued, whole, once every wave is done with the ring.
+    const bool chain = has_next && cur.nk >= 2 && nxt.nk >= 2;
     auto at_end = [&] {
       wait_lgkm0();
       block_barrier();
       if (has_next) {
-        e.setup(nxt.g, nxt.m0, nxt.n0, nxt.kbeg, nxt.klen);
-        if (nxt.nk > 0) e.issue_stage(0, 0);
-        if (nxt.nk > 1) e.issue_stage(1, 1);
+        if (nxt.nk > 0) e.issue_stage(dn, 0, 0);
+        if (nxt.nk > 1) e.issue_stage(dn, 1, 1);
       }
     };
-    if (cur.nk > 0) e.template run<S>(acc, cur.nk, stores, at_end);
+    if (cur.nk > 0) e.template run<S, true>(acc, dc, cur.nk, s0, stores, dn, chain, at_end);
     else at_end();
     store_wgrad8<TL::TM, TL::TN, TL::WTM, TL::WTN>(p, acc, cur.g, cur.m0, cur.n0, e.wm, e.wn,
                                                    e.lane, scr);
     if (!has_next) break;
+    s0 = chain ? (s0 + cur.nk) & 1 : 0;
+    ready = chain;
     l = ln;
     cur = nxt;
+    dc = dn;
     stores = true;
   }
 }
@@ -1352,7 +1392,7 @@ template <int KIND>
 hipError_t launch_rows(GemmArgs a, int64_t mcap, hipStream_t st) {
   if (a.block_m % kTallBlk == 0) {
     if (a.seg == nullptr) return hipErrorInvalidValue;
-    constexpr int cols = tile_cols<KIND>(tall8_bn<KIND>());
+    constexpr int cols = tile_cols<KIND>(kTall8BN);
     a.n_tiles_n = (int)((a.N + cols - 1) / cols);
     // sum over groups of ceil(nb_g / 3) <= (sum nb_g + 2 G) / 3, sum nb_g <= mcap / 128
     const int64_t tiles = (mcap / kTallBlk + 2 * (int64_t)a.G) / kTallMaxBlk + 1;

@@ -233,6 +233,10 @@ def _compare_layer(buf, f, b):
     (500, 512, 16, 4, 256, 1, 64, (0, 15)),
     (700, 384, 12, 6, 320, 2, 128, (4,)),
     (300, 256, 6, 2, 128, 0, 256, ()),
+    # more weight-gradient tiles (520 and 260) than persistent workgroups (256), skewed segments
+    # from empty to 24 contraction stages: tiles chained and not chained within one workgroup
+    (1500, 1024, 64, 4, 256, 1, 64, (3, 17, 40)),
+    (1500, 1024, 64, 4, 256, 1, 128, (5,)),
 ])
 def test_layer_parity(T, H, E, K, I, S, B, empty):
     log(f"layer T={T} H={H} E={E} K={K} I={I} S={S} B={B} empty={empty}")
