@@ -5,13 +5,16 @@
 // a workgroup tile belong to one expert and the grouped GEMM is scheduled like an ordinary GEMM.
 // Section A2 (MoE paragraph): each expert is a two-layer FFN with SwiGLU.
 //
-// On gfx950 the instruction is v_mfma_f32_32x32x16_bf16 (or 16x16x32 for 16-row tiles); the
-// workgroup tile is BM x BN x 64 with BM dividing block_m, four wavefronts, and both operands
-// staged through LDS as K-contiguous rows (operands stored the other way round in HBM are
-// transposed 8x8 in registers on the way in). Tiles are ordered so that consecutive ones share
-// an M-block (and an expert), and mapped to XCDs so that they also share an L2.
+// Three engines, by tile height (which must consist of whole blocks of one segment):
+//   - eight wavefronts (two per SIMD), tiles of 128-384 rows x 256 columns, for block_m a multiple
+//     of 128, and the persistent weight-gradient kernel (256 x 256 tiles of dW);
+//   - four wavefronts, 64 x 256 tiles, for block_m == 64;
+//   - four wavefronts with register-staged operands, 16- or 32-row tiles, for block_m 16 and 32.
+// The first two stage operands in LDS with the buffer->LDS DMA and read MN-major operands with
+// the transposing LDS read; the third loads through registers and transposes 8x8 in registers.
+// Tiles are mapped to XCDs so that tiles sharing an operand panel share an L2.
 //
-// Six kinds of tile share the engine:
+// Six kinds of tile share the engines:
 //   FwdGateUp   h = x_perm . W1[g]^T, fused a = silu(h_gate) * h_up (and h_save)
 //   FwdDown     y_perm = a . W2[g]^T
 //   DgradDown   da = dy_perm . W2[g], fused SwiGLU backward -> dh
@@ -716,10 +719,7 @@ __device__ __forceinline__ void pipe_tile(const GemmArgs& p, unsigned char* smem
   store_tile<KIND, TM, TN, WTM, WTN>(p, acc, g, m0, n0, wm, wn, lane);
 }
 
-// Tile shapes per kind. Row-grouped kinds: one tile shape per height (128, 256, 384 rows),
-// 4 x 1 waves over 128 columns; gate/up takes 64 gate + 64 up columns per tile.
-template <int KIND, int ROWS> struct TallTile { typedef Tile<ROWS, 128, 4, 32> type; };
-constexpr int kTallBN = 128;
+// Row-grouped 64-row tiles (block_m == 64) on the four-wavefront engine.
 typedef Tile<64, 256, 2, 64> Block64Tile;
 typedef Tile<256, 256, 2, 32> WgradTile;
 
@@ -1131,6 +1131,8 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
 constexpr int kTall8BN = 256;
 template <int ROWS> struct Tall8 { typedef Tile8<ROWS, kTall8BN, 4, 2> type; };
 
+// Row-grouped kinds with block_m a multiple of 128: every segment is cut into ceil(blocks / 3)
+// tiles of 1 to 3 whole 128-row blocks (the first `extra` tiles one block taller).
 template <int KIND>
 __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
@@ -1178,57 +1180,6 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   if (nblk == 3) pipe8_tile<KIND, Tall8<384>::type>(p, smem, g, m0, n0, 0, p.K);
   else if (nblk == 2) pipe8_tile<KIND, Tall8<256>::type>(p, smem, g, m0, n0, 0, p.K);
   else pipe8_tile<KIND, Tall8<128>::type>(p, smem, g, m0, n0, 0, p.K);
-}
-
-// Row-grouped kinds with block_m a multiple of 128: every segment is cut into ceil(blocks / 3)
-// tiles of 1 to 3 whole 128-row blocks (the first `extra` tiles one block taller).
-template <int KIND>
-__global__ __launch_bounds__(kThreads, 1) void ggemm_tall_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
-  int* pref = reinterpret_cast<int*>(smem);   // tiles before group g (reused by the DMA ring)
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int G = p.G;
-  if (tid < 64) {
-    int run = 0;
-    for (int base = 0; base < G; base += 64) {
-      const int g = base + lane;
-      const int nb = g < G ? (p.seg[g + 1] - p.seg[g]) / kTallBlk : 0;
-      int x = (nb + kTallMaxBlk - 1) / kTallMaxBlk;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
-      if (g < G) pref[g + 1] = run + x;
-      run += __shfl(x, 63, 64);
-    }
-    if (lane == 0) pref[0] = 0;
-  }
-  __syncthreads();
-  const int64_t n_tiles = pref[G];
-  const int64_t L = xcd_remap(blockIdx.x, n_tiles * p.n_tiles_n);
-  int g = 0, ti = 0, nt = 0;
-  if (L >= 0) {
-    ti = (int)(L / p.n_tiles_n);
-    nt = (int)(L % p.n_tiles_n);
-    int lo = 0, hi = G - 1;   // group of tile ti: largest g with pref[g] <= ti
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pref[mid] <= ti) lo = mid; else hi = mid - 1;
-    }
-    g = lo;
-  }
-  const int t0 = pref[g], ntg = pref[g + 1] - t0;
-  __syncthreads();   // pref is dead from here on: the DMA ring may overwrite it
-  if (L < 0) return;
-  const int nb = (p.seg[g + 1] - p.seg[g]) / kTallBlk;
-  const int local = ti - t0, base = nb / ntg, extra = nb % ntg;
-  const int blk0 = local * base + min(local, extra), nblk = base + (local < extra ? 1 : 0);
-  const int m0 = p.seg[g] + blk0 * kTallBlk;
-  const int n0 = nt * tile_cols<KIND>(kTallBN);
-  if (nblk == 3) pipe_tile<KIND, typename TallTile<KIND, 384>::type>(p, smem, g, m0, n0, 0, p.K);
-  else if (nblk == 2) pipe_tile<KIND, typename TallTile<KIND, 256>::type>(p, smem, g, m0, n0, 0, p.K);
-  else pipe_tile<KIND, typename TallTile<KIND, 128>::type>(p, smem, g, m0, n0, 0, p.K);
 }
 
 // Row-grouped kinds with 64-row tiles (block_m == 64): one block per tile, from tile_group.
