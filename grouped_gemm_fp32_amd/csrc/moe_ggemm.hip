@@ -389,8 +389,8 @@ __global__ __launch_bounds__(kThreads, 2) void ggemm_kernel(GemmArgs p) {
 // whatever address it loaded, and reads past the buffer resource's size return zero (tile tails
 // and segment ends need no special code). A ring of up to four stages of BK k.
 //   K-major operand (K contiguous in HBM): LDS [rows][BK]; 16-byte chunk c of row r sits at
-//     position c ^ swz(r) (swz = r & 7 with 8 chunks per row, (r >> 1) & 3 with 4), so the 32
-//     rows of a fragment read spread over all banks.
+//     position c ^ swz(r) (swz = (r >> 1) & 7 with 8 chunks per row, (r >> 2) & 3 with 4), so
+//     the rows of a fragment read spread over all banks.
 //   MN-major operand (rows contiguous in HBM, [k][rows]): LDS [BK][rows] as in HBM, chunk cc of
 //     k-row k stored at cc ^ ((k & 3) << 2); fragments come from ds_read_b64_tr_b16, which hands
 //     each lane 4 consecutive k of one column (within 16 lanes: lane i, item q <- lane 4q + i/4,
@@ -474,10 +474,15 @@ struct Tile {
 };
 
 // K-major LDS position of 16-byte chunk c of row r (an involution, so it also maps back).
+// gfx950 serves a 16-byte LDS read 16 lanes at a time from 64 banks (256 bytes): the 16 rows of
+// such a group must land on 16 distinct 16-byte bank slots. With 128-byte rows a slot is
+// (r & 1, position), so the position varies with r >> 1; with 64-byte rows it is (r & 3,
+// position) and varies with r >> 2. (Measured: keying on r & 7 instead gave 26x the conflict
+// cycles on the forward kernels.)
 template <int BK>
 __device__ __forceinline__ int kswz(int r, int c) {
-  if constexpr (BK == 64) return c ^ (r & 7);
-  else return c ^ ((r >> 1) & 3);
+  if constexpr (BK == 64) return c ^ ((r >> 1) & 7);
+  else return c ^ ((r >> 2) & 3);
 }
 
 // Epilogue shared by the engines: lane -> row, registers -> 4 consecutive columns per group.
@@ -958,15 +963,19 @@ struct Eng8 {
       return (uint32_t)((int64_t)i * (64 * NW / (BN / 8)) * p.ldb * 2);
     }
   }
-  // DMA instruction d (0..L-1) of stage kt of tile st into slot.
+  // DMA instruction d (0..L-1) of stage kt of tile st into slot. The B operand goes first: for
+  // the row-grouped kinds it is the expert weights, streamed once from HBM, so its requests miss
+  // L2 and need the longest head start; the A panel is shared by a segment's column tiles and
+  // mostly hits L2.
+  static constexpr int LB = TL::LB;
   __device__ __forceinline__ void dma_one(const Dma& st, int d, int kt, int slot) const {
     const uint32_t sl = lds_base + slot * STAGE;
-    if (d < LA) {
-      dma16(st.ra, st.a_off0 + uniform(kt * a_kstep + a_istride(d)), sl + (d * NW + wave) * 1024);
+    if (d < LB) {
+      dma16(st.rb, st.b_off0 + uniform(kt * b_kstep + b_istride(d)),
+            sl + A_BYTES + (d * NW + wave) * 1024);
     } else {
-      const int i = d - LA;
-      dma16(st.rb, st.b_off0 + uniform(kt * b_kstep + b_istride(i)),
-            sl + A_BYTES + (i * NW + wave) * 1024);
+      const int i = d - LB;
+      dma16(st.ra, st.a_off0 + uniform(kt * a_kstep + a_istride(i)), sl + (i * NW + wave) * 1024);
     }
   }
   __device__ __forceinline__ void issue_stage(const Dma& st, int kt, int slot) const {
