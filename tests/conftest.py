@@ -9,3 +9,8 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+    mutant = os.environ.get("ORACLE_MUTANT")
+    if mutant:   # only in the subprocesses test_oracle_mutations.py starts
+        sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+        import oracle_mutants
+        oracle_mutants.apply(mutant)
