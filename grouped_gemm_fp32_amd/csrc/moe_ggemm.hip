@@ -1211,6 +1211,7 @@ __global__ __launch_bounds__(kThreads, 1) void ggemm_block64_kernel(GemmArgs p) 
 // one workgroup per CU walking its XCD's tiles, and it issues the next tile's first two stages
 // before storing the current tile, so the stores drain under the next tile's MFMAs.
 typedef Tile8<256, 256, 4, 2> Wgrad8Tile;
+constexpr int kStoreNT = 2;   // cache-policy operand of buffer stores: non-temporal
 constexpr int kWgradScr = 4096;                     // epilogue staging per wavefront
 constexpr int kWgradStores = Wgrad8Tile::TM * (Wgrad8Tile::TN / 2) * 4;   // stores per wave per tile
 static_assert(2 * Wgrad8Tile::STAGE + Wgrad8Tile::NW * kWgradScr <= kLdsBytes, "LDS budget");
@@ -1239,7 +1240,9 @@ __device__ __forceinline__ void store_wgrad8(const GemmArgs& p, const f32x16_t (
                 (m < p.M && col < p.N) ? (uint32_t)(((int64_t)m * p.ldo + col) * 2) : 0x80000000u;
             typedef uint32_t v4_t __attribute__((ext_vector_type(4)));
             const v4_t v = {d.x, d.y, d.z, d.w};
-            __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+            // non-temporal: dW is written once and read by no later kernel here, so it should
+            // not evict the activation panels the next tiles read from L2
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStoreNT);
           });
     }
 }
@@ -1263,12 +1266,21 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) 
   int64_t l = (int64_t)xcd * per_x + blockIdx.x / kNumXcd;
   if (l >= lend) return;
   struct T { int g, m0, n0, kbeg, klen, nk; };
+  const bool m_fast = p.M <= p.N;
   auto decode = [&](int64_t L0) {
     T t;
     t.g = (int)(L0 / per_g);
     const int rem = (int)(L0 % per_g);
-    t.m0 = (rem / p.n_tiles_n) * TL::BM;
-    t.n0 = (rem % p.n_tiles_n) * TL::BN;
+    // Within a group the tiles along the smaller of M and N vary fastest: the 32 workgroups of
+    // an XCD then cover every panel of the operand with the smaller segment slice, which stays
+    // in L2 while the other operand's panels stream past once.
+    if (m_fast) {
+      t.m0 = (rem % p.n_tiles_m) * TL::BM;
+      t.n0 = (rem / p.n_tiles_m) * TL::BN;
+    } else {
+      t.m0 = (rem / p.n_tiles_n) * TL::BM;
+      t.n0 = (rem % p.n_tiles_n) * TL::BN;
+    }
     t.kbeg = ld_scalar(p.seg, t.g);
     t.klen = ld_scalar(p.seg, t.g + 1) - t.kbeg;
     t.nk = (t.klen + TL::BK - 1) / TL::BK;
