@@ -1,18 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE feed-forward hot path (dots.llm1 shapes) on one MI355X.
 
-A step is one pass of the whole path over one batch: routing (softmax, biased top-k, weights,
-counts), permutation into block-aligned expert segments, the grouped SwiGLU GEMMs (gate/up with the
-fused SwiGLU, down), the weighted combine, then the backward: combine backward, dgrad (down with
-the fused SwiGLU backward, gate/up), wgrad (down, gate/up) and the unpermute backward.
+Default workload (c2/c4 shapes): one step is one pass of the whole path over one batch:
+  - routing (softmax, biased top-k, weights, counts);
+  - permutation into block-aligned expert segments;
+  - the grouped SwiGLU GEMMs (gate/up with the fused SwiGLU, down);
+  - the weighted combine;
+  - then the backward: combine backward, dgrad (down with the fused SwiGLU backward, gate/up),
+    wgrad (down, gate/up) and the unpermute backward.
+It uses T=8192 tokens, hidden 4096, 128 experts top-6, intermediate 1408, block 128, with uniform
+routing (every expert gets exactly 384 rows). The routing stage runs on logits that encode that
+assignment, so the selection kernel runs but decides nothing else.
 
-Default workload: T=8192 tokens, hidden 4096, 128 experts top-6, intermediate 1408, block 128,
-uniform routing (every expert gets exactly 384 rows). The routing stage runs on logits that encode
-that assignment, so the selection kernel runs but decides nothing else.
+Other workloads (forward only, routing computed from x): `--workload c3` is the skewed full layer
+(T=16384, Zipf logit offsets, 2 shared experts, block 128); `--workload c5` is decode (T=256,
+random routing, 2 shared experts, block 16).
 
-Prints one JSON line: value = useful grouped-GEMM TFLOP/s of the whole step (padding excluded),
-with the dominant kernel's roofline (timed with HIP events on the launch stream) and the CPU
-oracle's throughput on a bounded sample of the same workload.
+Prints one JSON line. `value` is the useful grouped-GEMM TFLOP/s of the whole step (padding
+excluded). It also carries the dominant kernel's roofline, timed with HIP events on the launch
+stream, and the CPU oracle's throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -61,15 +67,17 @@ def load_traffic(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, x, w1, w2, logits, dy, sample_tokens):
-    """The CPU oracle, as it is, on the first `sample_tokens` tokens of the workload (fwd + bwd)."""
-    import numpy as np
+def _threads():
     from threadpoolctl import threadpool_info
+    return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+
+
+def cpu_baseline_fwd_bwd(cfg, x, w1, w2, logits, dy, sample_tokens):
+    """The CPU oracle, as it is, on the first `sample_tokens` tokens of the workload (fwd + bwd)."""
     from oracle import moe_oracle as O
 
     T = sample_tokens
     probs = O.softmax_probs(logits[:T])
-    idx, w = O.select_topk(probs, None, cfg.K)
     kw = dict(T=T, H=cfg.H, E=cfg.E, K=cfg.K, I=cfg.I, S=cfg.S)
     t0 = time.perf_counter()
     f = O.moe_forward(x[:T], w1, w2, B=cfg.block_m, probs=probs, **kw)
@@ -77,11 +85,46 @@ def cpu_baseline(cfg, x, w1, w2, logits, dy, sample_tokens):
     dt = time.perf_counter() - t0
     rows = T * cfg.K + cfg.S * T
     flops = 18.0 * cfg.H * cfg.I * rows
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"first {T} tokens of the workload ({rows} expert rows), forward + backward, "
                       f"float64 NumPy oracle; useful FLOPs / oracle seconds"}
+
+
+def cpu_baseline_fwd(cfg, x, w1, w2, wg, logit_bias, sel_bias, sample_tokens):
+    """The CPU oracle on the first `sample_tokens` tokens, forward from x (router included)."""
+    from oracle import moe_oracle as O
+
+    T = sample_tokens
+    kw = dict(T=T, H=cfg.H, E=cfg.E, K=cfg.K, I=cfg.I, S=cfg.S)
+    t0 = time.perf_counter()
+    O.moe_forward(x[:T], w1, w2, B=cfg.block_m, w_gate=wg, logit_bias=logit_bias,
+                  sel_bias=sel_bias, **kw)
+    dt = time.perf_counter() - t0
+    rows = T * cfg.K + cfg.S * T
+    flops = 6.0 * cfg.H * cfg.I * rows
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"first {T} tokens of the workload ({rows} expert rows), forward from x, "
+                      f"float64 NumPy oracle; useful grouped-GEMM FLOPs / oracle seconds"}
+
+
+def _time_steps(torch, np, step, nstages, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nstages + 1)]
+              for _ in range(steps)]
+    log(f"[bench] timing {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = [float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in events]))
+                for i in range(nstages)]
+    return wall * 1e3 / steps, stage_ms
 
 
 def main():
@@ -89,11 +132,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=("c2", "c3", "c5"), default="c2",
+                    help="c2: forward+backward at the uniform 8192-token shape (default); c3: skewed "
+                         "16384-token full layer forward; c5: 256-token decode forward")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, copy a cold buffer of this many MiB (a plain copy of known "
                          "size that scales the HBM byte counters)")
-    ap.add_argument("--cpu-sample", type=int, default=384,
-                    help="tokens of the workload the CPU oracle runs (0 = skip the CPU baseline)")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens of the workload the CPU oracle runs (0 = skip the CPU baseline); "
+                         "default 384 for c2, 256 for c3, all 256 for c5")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -105,46 +152,59 @@ def main():
     import numpy as np
     import torch
     import grouped_gemm_fp32_amd as M
-    from synth import get_config, draw_x, draw_w1_all, draw_w2_all, draw_dy, uniform_logits
+    import synth as Sy
 
     dev = "cuda:0"
-    cfg = get_config("c2")
+    cfg = Sy.get_config(args.workload)
     T, H, E, K, I, S, B = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.S, cfg.block_m
-    log(f"[bench] generating inputs T={T} H={H} E={E} K={K} I={I} S={S} B={B}")
+    log(f"[bench] {args.workload}: generating inputs T={T} H={H} E={E} K={K} I={I} S={S} B={B}")
     t0 = time.perf_counter()
-    x, w1, w2, dy, logits = draw_x(cfg), draw_w1_all(cfg), draw_w2_all(cfg), draw_dy(cfg), \
-        uniform_logits(cfg)
+    x, w1, w2 = Sy.draw_x(cfg), Sy.draw_w1_all(cfg), Sy.draw_w2_all(cfg)
+    fwd_bwd = args.workload == "c2"
+    if fwd_bwd:
+        dy, logits = Sy.draw_dy(cfg), Sy.uniform_logits(cfg)
+    else:
+        wg, lb, sb = Sy.draw_wg(cfg), Sy.draw_logit_bias(cfg), Sy.draw_sel_bias(cfg)
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
     s = M.make_shape(T, H, E, K, I, S, B)
-    buf = M.alloc_buffers(s, dev, backward=True)
-    X, W1, W2, DY = _bf(np, torch, x, dev), _bf(np, torch, w1, dev), _bf(np, torch, w2, dev), \
-        _bf(np, torch, dy, dev)
-    LG = torch.from_numpy(logits).to(dev)
+    b = M.alloc_buffers(s, dev, backward=fwd_bwd, save_h=fwd_bwd)
+    X, W1, W2 = _bf(np, torch, x, dev), _bf(np, torch, w1, dev), _bf(np, torch, w2, dev)
+    if fwd_bwd:
+        DY, LG = _bf(np, torch, dy, dev), torch.from_numpy(logits).to(dev)
+        route_args = (None, None, None, None, LG)
+    else:
+        WG = torch.from_numpy(wg).to(dev)
+        LB = torch.from_numpy(lb).to(dev) if lb is not None else None
+        SB = torch.from_numpy(sb).to(dev)
+        route_args = (X, WG, LB, SB, b["logits"])
     torch.cuda.synchronize()
 
-    stages = ["route", "permute", "fwd_gateup", "fwd_down", "combine", "combine_bwd",
-              "dgrad_down", "dgrad_gateup", "wgrad_down", "wgrad_gateup", "unpermute_bwd"]
-    b = buf
+    stages = ["route", "permute", "fwd_gateup", "fwd_down", "combine"]
+    if fwd_bwd:
+        stages += ["combine_bwd", "dgrad_down", "dgrad_gateup", "wgrad_down", "wgrad_gateup",
+                   "unpermute_bwd"]
+    h_save = b.get("h_save")
 
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record()
         mark(0)
-        M.moe_route(s, None, None, None, None, LG, b["probs"], b["topk_idx"], b["topk_w"],
-                    b["expert_counts"])
+        M.moe_route(s, *route_args, b["probs"], b["topk_idx"], b["topk_w"], b["expert_counts"])
         mark(1)
         M.moe_permute(s, b["topk_idx"], X, b["seg_offsets"], b["tile_group"], b["total_rows"],
                       b["row_token"], b["pos"], b["x_perm"], b["ws"])
         mark(2)
         M.grouped_gemm_fwd(s, M.MOE_FWD_GATEUP, b["x_perm"], b["seg_offsets"], b["tile_group"],
-                           b["total_rows"], W1, W2, b["h_save"], b["a"], b["y_perm"])
+                           b["total_rows"], W1, W2, h_save, b["a"], b["y_perm"])
         mark(3)
         M.grouped_gemm_fwd(s, M.MOE_FWD_DOWN, b["x_perm"], b["seg_offsets"], b["tile_group"],
-                           b["total_rows"], W1, W2, b["h_save"], b["a"], b["y_perm"])
+                           b["total_rows"], W1, W2, h_save, b["a"], b["y_perm"])
         mark(4)
         M.moe_combine(s, b["y_perm"], b["pos"], b["topk_w"], b["seg_offsets"], b["y"])
         mark(5)
+        if not fwd_bwd:
+            return
         M.moe_combine_bwd(s, DY, b["y_perm"], b["pos"], b["topk_w"], b["seg_offsets"],
                           b["row_token"], b["total_rows"], b["dy_perm"], b["dtopk_w"])
         for i, which in enumerate((M.MOE_DGRAD_DOWN, M.MOE_DGRAD_GATEUP, M.MOE_WGRAD_DOWN,
@@ -168,50 +228,58 @@ def main():
         log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + written")
         del src, flush, dst
     log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
+    step()
     torch.cuda.synchronize()
-    # routing sanity: the uniform assignment gives every expert T*K/E rows
-    counts = buf["expert_counts"].cpu().numpy()
-    assert np.all(counts == T * K // E), "uniform routing not reproduced"
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(12)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    stage_ms = {name: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in events]))
-                for i, name in enumerate(stages)}
+    counts = b["expert_counts"].cpu().numpy()
+    if fwd_bwd:   # the uniform assignment gives every expert T*K/E rows
+        assert np.all(counts == T * K // E), "uniform routing not reproduced"
+    ms_step, st_ms = _time_steps(torch, np, step, len(stages), args.steps, args.warmup)
+    stage_ms = dict(zip(stages, st_ms))
 
     rows = T * K + S * T                       # useful rows (padding excluded)
-    per_row = {"fwd_gateup": 4.0 * H * I, "fwd_down": 2.0 * H * I, "dgrad_down": 2.0 * H * I,
-               "dgrad_gateup": 4.0 * H * I, "wgrad_down": 2.0 * H * I, "wgrad_gateup": 4.0 * H * I}
+    per_row = {"fwd_gateup": 4.0 * H * I, "fwd_down": 2.0 * H * I}
+    if fwd_bwd:
+        per_row.update({"dgrad_down": 2.0 * H * I, "dgrad_gateup": 4.0 * H * I,
+                        "wgrad_down": 2.0 * H * I, "wgrad_gateup": 4.0 * H * I})
     step_flops = sum(per_row.values()) * rows
     value = step_flops / (ms_step * 1e-3) / 1e12
     dom = max(per_row, key=lambda k: stage_ms[k])
-    dom_flops = per_row[dom] * rows
-    achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
-    traffic = load_traffic(dom, "c2")
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": dom,
-                "traffic_gbs": (round(traffic / (stage_ms[dom] * 1e-3) / 1e9, 1)
-                                if traffic is not None else None),
-                "per_unit": f"{per_row[dom]:.0f} FLOP per routed row x {rows} rows per launch",
-                "avg_launch_ms": round(stage_ms[dom], 4)}
+    touched = int(np.sum(counts > 0)) + S      # groups whose weights are read
+    if args.workload == "c5":
+        # decode: each launch streams the weights of every touched expert once
+        wbytes = {"fwd_gateup": touched * 2 * I * H * 2, "fwd_down": touched * H * I * 2}
+        dom = max(wbytes, key=lambda k: stage_ms[k])
+        gbs = wbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "traffic": load_traffic(dom, args.workload), "kernel": dom,
+                    "per_unit": f"{wbytes[dom] // touched} weight bytes per touched expert x "
+                                f"{touched} experts per launch",
+                    "avg_launch_ms": round(stage_ms[dom], 4)}
+    else:
+        dom_flops = per_row[dom] * rows
+        achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
+        traffic = load_traffic(dom, args.workload)
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic, "kernel": dom,
+                    "traffic_gbs": (round(traffic / (stage_ms[dom] * 1e-3) / 1e9, 1)
+                                    if traffic is not None else None),
+                    "per_unit": f"{per_row[dom]:.0f} FLOP per useful row x {rows} rows per launch",
+                    "avg_launch_ms": round(stage_ms[dom], 4)}
+    desc = {"c2": "grouped-GEMM MoE FFN forward+backward, uniform routing (T=8192, hidden=4096, "
+                  "128 experts top-6, intermediate=1408, block_m=128, 384 rows per expert)",
+            "c3": "MoE FFN full layer forward from x, skewed routing (T=16384, hidden=4096, 128 "
+                  "experts top-6 with Zipf(1.1) logit offsets + 2 shared experts, intermediate=1408, "
+                  "block_m=128)",
+            "c5": "MoE FFN decode forward from x, random routing (T=256, hidden=4096, 128 experts "
+                  "top-6 + 2 shared experts, intermediate=1408, block_m=16)"}[args.workload]
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "grouped-GEMM MoE FFN forward+backward, uniform routing "
-                               "(T=8192, hidden=4096, 128 experts top-6, intermediate=1408, "
-                               "block_m=128, 384 rows per expert)",
-                   "T": T, "H": H, "E": E, "K": K, "I": I, "S": S, "block_m": B},
+        "config": {"workload": desc, "T": T, "H": H, "E": E, "K": K, "I": I, "S": S, "block_m": B},
         "roofline": roofline,
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
@@ -219,10 +287,14 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stages_tflops": {k: round(per_row[k] * rows / (stage_ms[k] * 1e-3) / 1e12, 1)
                           for k in per_row},
+        "experts_touched": touched,
     }
-    if args.cpu_sample > 0:
-        log(f"[bench] CPU oracle on {args.cpu_sample} tokens")
-        out["cpu_baseline"] = cpu_baseline(cfg, x, w1, w2, logits, dy, args.cpu_sample)
+    sample = args.cpu_sample if args.cpu_sample is not None else {"c2": 384, "c3": 256,
+                                                                   "c5": 256}[args.workload]
+    if sample > 0:
+        log(f"[bench] CPU oracle on {sample} tokens")
+        out["cpu_baseline"] = (cpu_baseline_fwd_bwd(cfg, x, w1, w2, logits, dy, sample) if fwd_bwd
+                               else cpu_baseline_fwd(cfg, x, w1, w2, wg, lb, sb, sample))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -123,7 +123,9 @@ moe_status_t moe_route(const moe_shape_t* s, const uint16_t* x, const float* w_g
   if (s->flags & MOE_PROBS_IN) {
     REQUIRE(probs);
   } else if (x) {
-    REQUIRE(w_gate);
+    REQUIRE_T(x);
+    REQUIRE_T(w_gate);
+    REQUIRE(logits);
   } else {
     REQUIRE(logits);
   }

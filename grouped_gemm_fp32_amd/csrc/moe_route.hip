@@ -4,11 +4,16 @@
 // computed in FP32 and picks the top-6 routed experts per token. Section A2, load-balancing
 // paragraph: a per-expert bias is added to the affinity scores to decide the top-k, and only there.
 //
-// One kernel does the whole router for a block of 32 tokens:
-//   1. logits[32, E] = fp32(x) . Wg^T with v_mfma_f32_32x32x2_f32 (fp32 inputs, fp32 accumulate),
-//      x and Wg staged through LDS in k-chunks of 64;
-//   2. one wavefront per token: softmax over E (wave reductions), key = p + b, K rounds of a
-//      wave-wide arg-max on a 64-bit (key, index) code, weights, per-expert counts.
+// Two kernels:
+//   1. router_logits_kernel: logits = x . Wg^T (+ logit_bias) in fp32 on the bf16 matrix unit. x is
+//      bf16, so exact; each fp32 weight is split exactly into three bf16 parts w = hi + mid + lo
+//      (24 significand bits), and three v_mfma_f32_32x32x16_bf16 per k-slice accumulate x*hi +
+//      x*mid + x*lo in fp32. Every product is exact in fp32, so this is the fp32 dot product up
+//      to summation order. One workgroup per 32 tokens x 32 experts; its four wavefronts take
+//      every fourth 64-k step and their partial sums are added in wavefront order (deterministic).
+//   2. route_kernel, a block of 32 tokens, one wavefront per token: softmax over E (wave
+//      reductions), key = p + b, K rounds of a wave-wide arg-max on a 64-bit (key, index) code,
+//      weights, per-expert counts.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -17,10 +22,9 @@ namespace {
 
 constexpr int kTokPerWg = 32;   // tokens per workgroup (the MFMA's 32 rows)
 constexpr int kRouteThreads = 256;
-constexpr int kKc = 64;          // k-chunk staged in LDS
 constexpr int kMaxE = 256;
 
-enum RouteMode { kFromX = 0, kFromLogits = 1, kFromProbs = 2 };
+enum RouteMode { kFromLogits = 1, kFromProbs = 2 };
 
 // Order-preserving map of a float key to uint32 (larger key -> larger code). -0 and +0 map to the
 // same code; NaN maps to 0, below every number.
@@ -31,16 +35,82 @@ __device__ __forceinline__ uint32_t key_code(float k) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---- 1. router logits ---------------------------------------------------------------------------
+constexpr int kLgTile = 32;   // tokens and experts per workgroup (the MFMA's 32 x 32)
+
+// Exact split of 8 fp32 values into three bf16 vectors with hi + mid + lo == w (each part is the
+// remainder rounded to bf16, so every subtraction is exact in fp32).
+__device__ __forceinline__ void split3(const float4& w0, const float4& w1, bf16x8_t& hi,
+                                       bf16x8_t& mid, bf16x8_t& lo) {
+  float r[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = (__bf16)r[i];
+    hi[i] = h;
+    r[i] -= (float)h;
+    const __bf16 m = (__bf16)r[i];
+    mid[i] = m;
+    r[i] -= (float)m;
+    lo[i] = (__bf16)r[i];
+  }
+}
+
+// logits[t0.., e0..] for a 32 x 32 tile. Lanes 0-31 hold token (A) and expert (B) rows r = lane;
+// within a 64-k step lane half h = lane >> 5 covers k = 32 h + 8 s .. +8 in slice s (the same
+// assignment for both operands, so each MFMA sums matching pairs and four slices cover the step).
+__global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
+    int T, int H, int E, const uint16_t* __restrict__ x, const float* __restrict__ wg,
+    const float* __restrict__ logit_bias, float* __restrict__ logits) {
+  __shared__ float red[4][kLgTile][kLgTile + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kLgTile, e0 = blockIdx.y * kLgTile;
+  const int r = lane & 31, h = lane >> 5;
+  const int t = min(t0 + r, T - 1), e = min(e0 + r, E - 1);   // rows past the end: not stored
+  const uint16_t* xr = x + (int64_t)t * H + h * 32;
+  const float* wr = wg + (int64_t)e * H + h * 32;
+  f32x16_t acc;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+  for (int step = wave; step < H / 64; step += 4) {   // H % 64 == 0
+    const int k = step * 64;
+    uint4 xa[4];
+    float4 wa[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const uint4*>(xr + k + 8 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wa[i] = *reinterpret_cast<const float4*>(wr + k + 4 * i);
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      bf16x8_t a, whi, wmid, wlo;
+      __builtin_memcpy(&a, &xa[sl], 16);
+      split3(wa[2 * sl], wa[2 * sl + 1], whi, wmid, wlo);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wlo, a, acc, 0, 0, 0);   // smallest first
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wmid, a, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(whi, a, acc, 0, 0, 0);
+    }
+  }
+  // D[expert][token]: lane -> token r, register q -> expert 8 (q / 4) + 4 h + q % 4.
+#pragma unroll
+  for (int q = 0; q < 16; ++q) red[wave][8 * (q >> 2) + 4 * h + (q & 3)][r] = acc[q];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kLgTile * kLgTile; idx += kRouteThreads) {
+    const int el = idx / kLgTile, tl = idx % kLgTile;
+    if (t0 + tl < T && e0 + el < E) {
+      float z = red[0][el][tl] + red[1][el][tl] + red[2][el][tl] + red[3][el][tl];
+      if (logit_bias) z += logit_bias[e0 + el];
+      logits[(int64_t)(t0 + tl) * E + e0 + el] = z;
+    }
+  }
+}
+
+// ---- 2. softmax, biased top-K, weights, counts -----------------------------------------------------
 template <int MODE>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    int T, int H, int E, int K, uint32_t flags, const uint16_t* __restrict__ x,
-    const float* __restrict__ wg, const float* __restrict__ logit_bias,
-    const float* __restrict__ sel_bias, float* __restrict__ logits, float* __restrict__ probs,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts) {
-  // LDS: staging for the GEMM (x chunk 32 x 64, Wg chunk E x 64, padded rows), then reused for
-  // the [32][E] score tile.
-  __shared__ float sx[kTokPerWg][kKc + 4];
-  __shared__ float sw[kMaxE][kKc + 4];
+    int T, int E, int K, uint32_t flags, const float* __restrict__ sel_bias,
+    const float* __restrict__ logits, float* __restrict__ probs, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ counts) {
+  // LDS: the [32][E] fp32 score tile.
+  __shared__ float score[kTokPerWg * (kMaxE + 1)];
   __shared__ int hist[kMaxE];
 
   const int tid = threadIdx.x;
@@ -51,85 +121,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 
   for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
 
-  // score[tok][e] lives in sw's storage after the GEMM: [32][E] floats.
-  float* score = &sw[0][0];
-  const int sstride = kMaxE + 1;  // 32 * 257 floats fits in sw (256 * 68)
+  const int sstride = kMaxE + 1;
 
-  if (MODE == kFromX) {
-    // ---- 1. logits = x . Wg^T on fp32 MFMA -------------------------------------------------
-    // Wave w owns experts [w*32, w*32+32) and, for E > 128, [128 + w*32, ...).
-    const int n_et = (E + 31) / 32;  // expert tiles of 32
-    f32x16_t acc[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
-
-    for (int k0 = 0; k0 < H; k0 += kKc) {
-      // x chunk: 32 tokens x 64 k (bf16 -> fp32, exact). 256 threads x 8 elements.
-      {
-        const int tk = tid >> 3, c = (tid & 7) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (tk < ntok) v = *reinterpret_cast<const uint4*>(x + (int64_t)(t0 + tk) * H + k0 + c);
-        float* d = &sx[tk][c];
-        d[0] = lo_bf(v.x); d[1] = hi_bf(v.x); d[2] = lo_bf(v.y); d[3] = hi_bf(v.y);
-        d[4] = lo_bf(v.z); d[5] = hi_bf(v.z); d[6] = lo_bf(v.w); d[7] = hi_bf(v.w);
-      }
-      // Wg chunk: E x 64 fp32, 16 floats (4 x float4) per thread-iteration.
-      for (int idx = tid; idx < E * (kKc / 4); idx += kRouteThreads) {
-        const int e = idx / (kKc / 4), c = (idx % (kKc / 4)) * 4;
-        const float4 v = *reinterpret_cast<const float4*>(wg + (int64_t)e * H + k0 + c);
-        *reinterpret_cast<float4*>(&sw[e][c]) = v;
-      }
-      __syncthreads();
-      // 64 k per chunk = 16 groups of 4; lane l takes k = 4*(l/32) + {0..3} of an 8-wide group,
-      // the same mapping for both operands, so each MFMA sums a consistent pair of k.
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int et = wave + q * 4;
-        if (et < n_et) {
-          const int e = et * 32 + (lane & 31);
-          const bool ev = e < E;
-#pragma unroll
-          for (int kg = 0; kg < kKc; kg += 8) {
-            const int kk = kg + (lane >> 5) * 4;
-            const float4 a4 = *reinterpret_cast<const float4*>(&sx[lane & 31][kk]);
-            float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (ev) b4 = *reinterpret_cast<const float4*>(&sw[e][kk]);
-            acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(b4.x, a4.x, acc[q], 0, 0, 0);
-            acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(b4.y, a4.y, acc[q], 0, 0, 0);
-            acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(b4.z, a4.z, acc[q], 0, 0, 0);
-            acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(b4.w, a4.w, acc[q], 0, 0, 0);
-          }
-        }
-      }
-      __syncthreads();
-    }
-    // D[e][tok]: lane -> token (lane & 31), registers -> 4 consecutive experts per group of 4.
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int et = wave + q * 4;
-      if (et < n_et) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int e = et * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int tk = lane & 31;
-          if (e < E) {
-            float z = acc[q][r];
-            if (logit_bias) z += logit_bias[e];
-            score[tk * sstride + e] = z;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    if (logits) {
-      for (int idx = tid; idx < ntok * E; idx += kRouteThreads) {
-        const int tk = idx / E, e = idx % E;
-        logits[(int64_t)(t0 + tk) * E + e] = score[tk * sstride + e];
-      }
-    }
-  } else {
+  {
     const float* src = MODE == kFromLogits ? logits : probs;
     for (int idx = tid; idx < ntok * E; idx += kRouteThreads) {
       const int tk = idx / E, e = idx % E;
@@ -262,15 +256,19 @@ hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg
   }
   const dim3 grid((unsigned)((s.T + kTokPerWg - 1) / kTokPerWg)), block(kRouteThreads);
   if (s.flags & MOE_PROBS_IN) {
-    hipLaunchKernelGGL(route_kernel<kFromProbs>, grid, block, 0, st, s.T, s.H, s.E, s.K, s.flags,
-                       x, wg, logit_bias, sel_bias, logits, probs, topk_idx, topk_w, counts);
-  } else if (x) {
-    hipLaunchKernelGGL(route_kernel<kFromX>, grid, block, 0, st, s.T, s.H, s.E, s.K, s.flags, x,
-                       wg, logit_bias, sel_bias, logits, probs, topk_idx, topk_w, counts);
-  } else {
-    hipLaunchKernelGGL(route_kernel<kFromLogits>, grid, block, 0, st, s.T, s.H, s.E, s.K, s.flags,
-                       x, wg, logit_bias, sel_bias, logits, probs, topk_idx, topk_w, counts);
+    hipLaunchKernelGGL(route_kernel<kFromProbs>, grid, block, 0, st, s.T, s.E, s.K, s.flags,
+                       sel_bias, logits, probs, topk_idx, topk_w, counts);
+    return hipGetLastError();
   }
+  if (x) {
+    const dim3 lg((unsigned)((s.T + kLgTile - 1) / kLgTile), (unsigned)((s.E + kLgTile - 1) / kLgTile));
+    hipLaunchKernelGGL(router_logits_kernel, lg, block, 0, st, s.T, s.H, s.E, x, wg, logit_bias,
+                       logits);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(route_kernel<kFromLogits>, grid, block, 0, st, s.T, s.E, s.K, s.flags, sel_bias,
+                     logits, probs, topk_idx, topk_w, counts);
   return hipGetLastError();
 }
 

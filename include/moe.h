@@ -99,10 +99,12 @@ size_t moe_workspace_size(const moe_shape_t* shape);
  *                 lower expert index, NaN below every number; slots in rank order
  *   topk_w[T,K] = p_e / sum of the selected p (MOE_NORM_TOPK) or p_e: the bias never enters it
  *   expert_counts[E] = tokens routed to each expert (TR section 6)
- * Modes: x != NULL computes logits (written if `logits` != NULL); x == NULL reads `logits` as the
- * input; flag MOE_PROBS_IN reads `probs` as the input (x, w_gate, logits unused).
- * Optional (may be NULL): logit_bias, sel_bias (= 0), logits (when x != NULL), probs (unless
- * MOE_PROBS_IN), expert_counts. Required: topk_idx, topk_w; w_gate when x != NULL.
+ * Modes: x != NULL computes logits into `logits` (one kernel), then routes from them (a second);
+ * x == NULL reads `logits` as the input; flag MOE_PROBS_IN reads `probs` as the input (x, w_gate,
+ * logits unused).
+ * Optional (may be NULL): logit_bias, sel_bias (= 0), probs (unless MOE_PROBS_IN), expert_counts.
+ * Required: topk_idx, topk_w; logits unless MOE_PROBS_IN; with x != NULL, x and w_gate non-NULL
+ * and 16-byte aligned (else MOE_ERR_INVALID_ARG).
  */
 moe_status_t moe_route(const moe_shape_t* shape, const uint16_t* x, const float* w_gate,
                        const float* logit_bias, const float* sel_bias, float* logits, float* probs,

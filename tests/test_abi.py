@@ -67,8 +67,9 @@ def test_shape_validation(lib):
 def test_null_required_pointers(lib):
     s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
     d = ctypes.c_void_p(16)
-    # moe_route: topk outputs required; x given needs w_gate; x NULL needs logits
-    assert lib.moe_route(ctypes.byref(s), d, None, None, None, None, None, d, d, None, None) == -1
+    # moe_route: topk outputs required; x given needs w_gate and logits; x NULL needs logits
+    assert lib.moe_route(ctypes.byref(s), d, None, None, None, d, None, d, d, None, None) == -1
+    assert lib.moe_route(ctypes.byref(s), d, d, None, None, None, None, d, d, None, None) == -1
     assert lib.moe_route(ctypes.byref(s), None, None, None, None, None, None, d, d, None, None) == -1
     assert lib.moe_route(ctypes.byref(s), None, None, None, None, d, None, None, d, None, None) == -1
     s_probs = M.make_shape(8, 256, 8, 2, 128, 1, 16, flags=M.MOE_PROBS_IN)
@@ -120,6 +121,11 @@ def test_gemm_tensors_must_be_16_byte_aligned(lib):
         a = [d] * 13
         a[i] = odd
         assert lib.grouped_gemm_bwd(ctypes.byref(s), M.MOE_DGRAD | M.MOE_WGRAD, *a, None) == -1
+        assert "aligned" in M.moe_last_error()
+    for i in (0, 1):   # moe_route from x: x, w_gate (read with 16-byte vector loads)
+        a = [d, d, None, None, d, None, d, d, None]
+        a[i] = odd
+        assert lib.moe_route(ctypes.byref(s), *a, None) == -1
         assert "aligned" in M.moe_last_error()
 
 
