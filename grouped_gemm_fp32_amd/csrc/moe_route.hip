@@ -11,17 +11,18 @@
 //      x*mid + x*lo in fp32. Every product is exact in fp32, so this is the fp32 dot product up
 //      to summation order. One workgroup per 32 tokens x 32 experts; its four wavefronts take
 //      every fourth 64-k step and their partial sums are added in wavefront order (deterministic).
-//   2. route_kernel, a block of 32 tokens, one wavefront per token: softmax over E (wave
-//      reductions), key = p + b, K rounds of a wave-wide arg-max on a 64-bit (key, index) code,
-//      weights, per-expert counts.
+//   2. route_kernel, one wavefront per token at a time (a few consecutive tokens each): softmax
+//      over E, key = p + b, K rounds of a wave-wide arg-max on a 64-bit (key, index) code,
+//      weights, per-expert counts (an LDS histogram per workgroup, then one atomic per expert).
+//      The cross-lane reductions use DPP and permlane swaps, not the LDS crossbar.
 #include "moe_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTokPerWg = 32;   // tokens per workgroup (the MFMA's 32 rows)
 constexpr int kRouteThreads = 256;
+constexpr int kRouteWaves = 2048;   // target wavefront count of the routing kernel
 constexpr int kMaxE = 256;
 
 enum RouteMode { kFromLogits = 1, kFromProbs = 2 };
@@ -104,69 +105,106 @@ __global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
 }
 
 // ---- 2. softmax, biased top-K, weights, counts -----------------------------------------------------
+// Cross-lane steps without the LDS crossbar: DPP for partners within a row of 16 lanes, and
+// gfx950's permlane swaps for rows 16 and 32 apart. Each step combines two disjoint, equal-size
+// lane groups that are already uniform, so after six steps every lane holds the reduction over
+// all 64 lanes (and the same bits on every lane, since the combining order is fixed).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// The two values a permlane swap leaves: (own row group's, partner row group's), 16 or 32 apart.
+__device__ __forceinline__ void swap16(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  a = r[0]; b = r[1];
+}
+__device__ __forceinline__ void swap32(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  a = r[0]; b = r[1];
+}
+
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, __uint_as_float(dpp<kDppXor1>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp<kDppXor2>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(v))));
+  v = op(v, __uint_as_float(dpp<kDppMirror>(__float_as_uint(v))));
+  uint32_t a, b;
+  swap16(__float_as_uint(v), a, b);
+  v = op(__uint_as_float(a), __uint_as_float(b));
+  swap32(__float_as_uint(v), a, b);
+  return op(__uint_as_float(a), __uint_as_float(b));
+}
+
+// Larger of two (code, ~index) pairs: higher code, then lower expert index.
+__device__ __forceinline__ void pair_max(uint32_t& hi, uint32_t& lo, uint32_t ohi, uint32_t olo) {
+  if (ohi > hi || (ohi == hi && olo > lo)) { hi = ohi; lo = olo; }
+}
+__device__ __forceinline__ void wave_argmax(uint32_t& hi, uint32_t& lo) {
+  pair_max(hi, lo, dpp<kDppXor1>(hi), dpp<kDppXor1>(lo));
+  pair_max(hi, lo, dpp<kDppXor2>(hi), dpp<kDppXor2>(lo));
+  pair_max(hi, lo, dpp<kDppHalfMirror>(hi), dpp<kDppHalfMirror>(lo));
+  pair_max(hi, lo, dpp<kDppMirror>(hi), dpp<kDppMirror>(lo));
+  uint32_t ah, bh, al, bl;
+  swap16(hi, ah, bh); swap16(lo, al, bl);
+  hi = ah; lo = al; pair_max(hi, lo, bh, bl);
+  swap32(hi, ah, bh); swap32(lo, al, bl);
+  hi = ah; lo = al; pair_max(hi, lo, bh, bl);
+}
+
+// Each wavefront routes `tpw` consecutive tokens, one at a time, with the next token's scores
+// loaded while the current one is processed. Lane l holds experts l, l + 64, l + 128, l + 192.
 template <int MODE>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    int T, int E, int K, uint32_t flags, const float* __restrict__ sel_bias,
+    int T, int E, int K, int tpw, uint32_t flags, const float* __restrict__ sel_bias,
     const float* __restrict__ logits, float* __restrict__ probs, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ counts) {
-  // LDS: the [32][E] fp32 score tile.
-  __shared__ float score[kTokPerWg * (kMaxE + 1)];
   __shared__ int hist[kMaxE];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int t0 = blockIdx.x * kTokPerWg;
-  const int ntok = min(kTokPerWg, T - t0);
-
   for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
+  __syncthreads();
 
-  const int sstride = kMaxE + 1;
-
-  {
-    const float* src = MODE == kFromLogits ? logits : probs;
-    for (int idx = tid; idx < ntok * E; idx += kRouteThreads) {
-      const int tk = idx / E, e = idx % E;
-      score[tk * sstride + e] = src[(int64_t)(t0 + tk) * E + e];
-    }
-    __syncthreads();
-  }
-
-  // ---- 2. per token: softmax, biased top-K, weights, counts (one wavefront per token) --------
   const bool norm = (flags & MOE_NORM_TOPK) != 0;
+  const float* src = MODE == kFromLogits ? logits : probs;
   float bias[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int e = lane + 64 * s;
     bias[s] = (e < E && sel_bias) ? sel_bias[e] : 0.0f;
   }
-  for (int tk = wave; tk < ntok; tk += kRouteThreads / 64) {
-    const int t = t0 + tk;
-    float p[4];
-    if (MODE == kFromProbs) {
+  const int tb = (blockIdx.x * (kRouteThreads / 64) + wave) * tpw;
+  const int tn = min(T, tb + tpw);
+  auto load = [&](int t, float (&z)[4]) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int e = lane + 64 * s;
-        p[s] = e < E ? score[tk * sstride + e] : 0.0f;
-      }
-    } else {
-      float z[4];
+    for (int s = 0; s < 4; ++s) {
+      const int e = lane + 64 * s;
+      z[s] = (t < tn && e < E) ? src[(int64_t)t * E + e] : 0.0f;
+    }
+  };
+  float nxt[4];
+  load(tb, nxt);
+  for (int t = tb; t < tn; ++t) {
+    float p[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) p[s] = nxt[s];
+    load(t + 1, nxt);
+    if (MODE == kFromLogits) {
       float m = -INFINITY;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int e = lane + 64 * s;
-        z[s] = e < E ? score[tk * sstride + e] : -INFINITY;
-        m = fmaxf(m, z[s]);
-      }
-      m = wave_max(m);
+      for (int s = 0; s < 4; ++s)
+        if (lane + 64 * s < E) m = fmaxf(m, p[s]);
+      m = wave_reduce(m, [](float a, float b) { return fmaxf(a, b); });
       float sum = 0.0f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int e = lane + 64 * s;
-        p[s] = e < E ? expf(z[s] - m) : 0.0f;
+        p[s] = lane + 64 * s < E ? expf(p[s] - m) : 0.0f;
         sum += p[s];
       }
-      sum = wave_sum(sum);
+      sum = wave_reduce(sum, [](float a, float b) { return a + b; });
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int e = lane + 64 * s;
@@ -197,19 +235,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
             if (bi == 0xffffffffu || code[s] > bc) { bc = code[s]; bi = (uint32_t)e; }
           }
         }
-        // Wave arg-max on (code, ~index): a lane without a candidate offers (0, 0), which loses
-        // to every real expert, NaN keys (code 0) included.
+        // A lane without a candidate offers (0, 0), which loses to every real expert, NaN keys
+        // (code 0) included.
         uint32_t hi = bc, lo = ~bi;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const uint32_t ohi = __shfl_xor(hi, o, 64), olo = __shfl_xor(lo, o, 64);
-          if (ohi > hi || (ohi == hi && olo > lo)) { hi = ohi; lo = olo; }
-        }
-        const int e = (int)(~lo);
+        wave_argmax(hi, lo);
+        const int e = __builtin_amdgcn_readfirstlane((int)(~lo));
         if ((e & 63) == lane) taken |= 1u << (e >> 6);
         const int s = e >> 6;
         const float pv = s == 0 ? p[0] : s == 1 ? p[1] : s == 2 ? p[2] : p[3];
-        const float pe = __shfl(pv, e & 63, 64);
+        const float pe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pv), e & 63));
         sel_e[j] = e;
         sel_p[j] = pe;
         wsum += pe;  // slot order
@@ -254,9 +288,13 @@ hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg
     hipError_t e = launch_fill_i32(counts, 0, s.E, st);
     if (e != hipSuccess) return e;
   }
-  const dim3 grid((unsigned)((s.T + kTokPerWg - 1) / kTokPerWg)), block(kRouteThreads);
+  // About 2048 wavefronts (8 per CU) with whole tokens each; at most 512 workgroups, so the
+  // per-workgroup count merges stay few.
+  const int tpw = (int)((s.T + kRouteWaves - 1) / kRouteWaves);   // T >= 1 here
+  const int toks_per_wg = tpw * (kRouteThreads / 64);
+  const dim3 grid((unsigned)((s.T + toks_per_wg - 1) / toks_per_wg)), block(kRouteThreads);
   if (s.flags & MOE_PROBS_IN) {
-    hipLaunchKernelGGL(route_kernel<kFromProbs>, grid, block, 0, st, s.T, s.E, s.K, s.flags,
+    hipLaunchKernelGGL(route_kernel<kFromProbs>, grid, block, 0, st, s.T, s.E, s.K, tpw, s.flags,
                        sel_bias, logits, probs, topk_idx, topk_w, counts);
     return hipGetLastError();
   }
@@ -267,8 +305,8 @@ hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(route_kernel<kFromLogits>, grid, block, 0, st, s.T, s.E, s.K, s.flags, sel_bias,
-                     logits, probs, topk_idx, topk_w, counts);
+  hipLaunchKernelGGL(route_kernel<kFromLogits>, grid, block, 0, st, s.T, s.E, s.K, tpw, s.flags,
+                     sel_bias, logits, probs, topk_idx, topk_w, counts);
   return hipGetLastError();
 }
 
