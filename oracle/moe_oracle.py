@@ -14,13 +14,17 @@ What it computes, and where that is stated (TR = the dots.llm1 Technical Report 
     block size so every tile of rows belongs to one expert. Padding and permutation only reorganise
     the work; the result is the plain MoE definition.
   * TR section 6 "MoE analysis": the per-expert token count N_{E_i} behind the expert-load figure.
+  * TR section A2, load-balancing paragraph, again: the per-expert bias is adjusted during training
+    to keep the expert loads balanced (the router backward and the bias update below).
 
 Where the pages leave a step open the oracle takes one reading, stated at the function:
 softmax affinities over the routed experts; the bias added to the probability; weights renormalised
 over the K selected experts (optional); ties to the lower expert index, NaN below every number;
 SwiGLU(x) = W2 (silu(W1_gate x) * W1_up x) with no biases; shared experts weight 1; ascending token
 order inside a segment with shared groups last; bf16 round-to-nearest-even at the stored tensors
-(h, a, y_perm, y, dy_perm, dh, dx_perm, dx, dW1, dW2) and fp32 for logits, probabilities and weights.
+(h, a, y_perm, y, dy_perm, dh, dx_perm, dx, dW1, dW2) and fp32 for logits, probabilities and weights;
+the selection passes no gradient and the selection bias gets none; the bias moves by a fixed step
+gamma toward the mean load (sign of mean load minus the expert's load).
 
 Arithmetic is float64 (products of bf16 values are exact in it); rounding to bf16 or fp32 happens
 only where the path stores a tensor. Passing ``rnd=None`` turns every bf16 rounding off, which the
@@ -387,6 +391,66 @@ def unpermute_backward(dx_perm, pos, seg_offsets, T: int, E: int, S: int, rnd="b
     for s in range(S):
         acc += dx_perm[seg[E + s]: seg[E + s] + T]
     return R(acc)
+
+
+# ------------------------------------------------------------------------------------------------
+# Router backward and the load-balancing bias update (TR section A2, load-balancing paragraph)
+# ------------------------------------------------------------------------------------------------
+def route_backward(probs, topk_idx, dtopk_w, normalize: bool = True) -> np.ndarray:
+    """dlogits[T,E]: gradient of a loss with respect to the router logits, given dL/dw = dtopk_w.
+
+    The routing weights depend on the logits only through the softmax probabilities p (the
+    selection is piecewise constant, so it passes no gradient, and the selection bias, which the
+    pages use only to pick the top-k, gets none). Two chain-rule steps, in float64:
+      1. g = dL/dp, zero off the K selected experts. Renormalised weights w_j = p_{e_j} / S with
+         S = sum_i p_{e_i}: dw_j/dp_{e_k} = (delta_jk - w_j) / S, so g_{e_k} = (dw_k - sum_j w_j
+         dw_j) / S. Unnormalised weights w_j = p_{e_j}: g_{e_k} = dw_k.
+      2. Softmax: dp_e/dz_f = p_e (delta_ef - p_f), so dz_f = p_f (g_f - sum_e p_e g_e).
+    Rounded once to fp32.
+    """
+    p = np.asarray(probs, dtype=np.float32).astype(np.float64)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    dw = np.asarray(dtopk_w, dtype=np.float32).astype(np.float64)
+    T, E = p.shape
+    sel_p = np.take_along_axis(p, idx, axis=1)
+    if normalize:
+        S = sel_p.sum(axis=1, keepdims=True)
+        w = sel_p / S
+        g_sel = (dw - (w * dw).sum(axis=1, keepdims=True)) / S
+    else:
+        g_sel = dw
+    g = np.zeros((T, E))
+    np.put_along_axis(g, idx, g_sel, axis=1)
+    dz = p * (g - (p * g).sum(axis=1, keepdims=True))
+    return dz.astype(np.float32)
+
+
+def router_weight_grad(dlogits, x_bits) -> np.ndarray:
+    """dWg[E,H] = dlogits^T x (the logits are x . Wg^T), float64 rounded once to fp32."""
+    dz = np.asarray(dlogits, dtype=np.float32).astype(np.float64)
+    return (dz.T @ _as_values(x_bits)).astype(np.float32)
+
+
+def router_input_grad(dlogits, w_gate) -> np.ndarray:
+    """The router's share of dx: dlogits Wg [T,H], float64 rounded once to fp32."""
+    dz = np.asarray(dlogits, dtype=np.float32).astype(np.float64)
+    return (dz @ np.asarray(w_gate, dtype=np.float32).astype(np.float64)).astype(np.float32)
+
+
+def bias_update(sel_bias, counts, T: int, K: int, gamma: float) -> np.ndarray:
+    """One step of the aux-loss-free balance: b_e + gamma * sign(mean load - c_e), in fp32.
+
+    The pages say only that each expert's bias is adjusted during training to keep the load
+    balanced. Reading (the update of the cited aux-loss-free method): an expert with fewer than
+    the mean T*K/E routed tokens has its bias raised by the update speed gamma, one with more has
+    it lowered, one at the mean keeps it. The comparison is exact in integers (T*K vs E*c_e) and
+    the update is one fp32 addition.
+    """
+    b = np.asarray(sel_bias, dtype=np.float32)
+    c = np.asarray(counts, dtype=np.int64)
+    E = b.shape[0]
+    sgn = np.sign(T * K - E * c).astype(np.float32)
+    return (b + np.float32(gamma) * sgn).astype(np.float32)
 
 
 # ------------------------------------------------------------------------------------------------

@@ -15,7 +15,7 @@ from oracle import moe_oracle as O
 _ORIG = {name: getattr(O, name) for name in (
     "softmax_probs", "selection_keys", "select_topk", "expert_counts", "permute_maps",
     "expert_ffn_rows", "combine", "combine_backward", "swiglu_backward", "expert_ffn_dgrad",
-    "expert_ffn_wgrad", "round_bf16")}
+    "expert_ffn_wgrad", "round_bf16", "route_backward", "router_weight_grad", "bias_update")}
 
 
 # --- routing --------------------------------------------------------------------------------------
@@ -140,6 +140,45 @@ def dy_perm_unweighted(dy_bits_or_vals, y_perm, pos, topk_w, *args, **kwargs):
     return dy_perm, dw
 
 
+# --- router backward and bias update ---------------------------------------------------------------
+def route_bwd_uncentred(probs, topk_idx, dtopk_w, normalize=True):
+    # the renormalisation's -sum_j w_j dw_j term dropped (as if dw/dp were 1/S on the diagonal)
+    p = np.asarray(probs, np.float32).astype(np.float64)
+    idx = np.asarray(topk_idx, np.int64)
+    dw = np.asarray(dtopk_w, np.float32).astype(np.float64)
+    sel = np.take_along_axis(p, idx, axis=1)
+    g_sel = dw / sel.sum(axis=1, keepdims=True) if normalize else dw
+    g = np.zeros_like(p)
+    np.put_along_axis(g, idx, g_sel, axis=1)
+    return (p * (g - (p * g).sum(axis=1, keepdims=True))).astype(np.float32)
+
+
+def route_bwd_no_softmax(probs, topk_idx, dtopk_w, normalize=True):
+    # dL/dp returned as if it were dL/dz (softmax Jacobian skipped)
+    p = np.asarray(probs, np.float32).astype(np.float64)
+    idx = np.asarray(topk_idx, np.int64)
+    dw = np.asarray(dtopk_w, np.float32).astype(np.float64)
+    sel = np.take_along_axis(p, idx, axis=1)
+    if normalize:
+        S = sel.sum(axis=1, keepdims=True)
+        g_sel = (dw - (sel / S * dw).sum(axis=1, keepdims=True)) / S
+    else:
+        g_sel = dw
+    g = np.zeros_like(p)
+    np.put_along_axis(g, idx, g_sel, axis=1)
+    return g.astype(np.float32)
+
+
+def router_weight_grad_mean(dlogits, x_bits):
+    # averaged over the tokens instead of summed
+    dw = _ORIG["router_weight_grad"](dlogits, x_bits)
+    return (dw / np.float32(np.asarray(dlogits).shape[0])).astype(np.float32)
+
+
+def bias_update_sign_flipped(sel_bias, counts, T, K, gamma):
+    return _ORIG["bias_update"](sel_bias, counts, T, K, -gamma)
+
+
 # --- number format ---------------------------------------------------------------------------------
 def round_toward_zero(v):
     # truncate to bf16 instead of rounding to nearest even
@@ -192,6 +231,17 @@ MUTANTS = {
                        ["test_oracle_backward.py::test_fd_dtopk_w"]),
     "dy_perm_unweighted": ("combine_backward", dy_perm_unweighted,
                            ["test_oracle_backward.py::test_fd_dx_dw1_dw2_dw"]),
+    "route_bwd_uncentred": ("route_backward", route_bwd_uncentred,
+                            ["test_oracle_route_bwd.py::test_route_backward_matches_autograd",
+                             "test_oracle_route_bwd.py::test_route_backward_finite_differences"]),
+    "route_bwd_no_softmax": ("route_backward", route_bwd_no_softmax,
+                             ["test_oracle_route_bwd.py::test_route_backward_matches_autograd",
+                              "test_oracle_route_bwd.py::test_route_backward_invariants"]),
+    "router_weight_grad_mean": ("router_weight_grad", router_weight_grad_mean,
+                                ["test_oracle_route_bwd.py::test_router_weight_and_input_grads_match_autograd"]),
+    "bias_update_sign_flipped": ("bias_update", bias_update_sign_flipped,
+                                 ["test_oracle_route_bwd.py::test_bias_update_hand_worked",
+                                  "test_oracle_route_bwd.py::test_bias_update_is_one_fp32_add"]),
     "round_toward_zero": ("round_bf16", round_toward_zero,
                           ["test_oracle_numerics.py::test_round_bf16_known_values",
                            "test_oracle_numerics.py::test_round_bf16_matches_torch_on_fp32_inputs"]),
