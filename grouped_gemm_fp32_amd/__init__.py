@@ -17,7 +17,8 @@ __all__ = [
     "MOE_WGRAD",
     "moe_abi_version", "moe_status_string", "moe_last_error", "moe_row_capacity",
     "moe_workspace_size", "moe_route", "moe_permute", "grouped_gemm_fwd", "grouped_gemm_bwd",
-    "moe_combine", "moe_combine_bwd", "moe_unpermute_bwd", "make_shape", "alloc_buffers",
+    "moe_combine", "moe_combine_bwd", "moe_unpermute_bwd", "moe_route_bwd", "moe_bias_update",
+    "make_shape", "alloc_buffers",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +77,8 @@ _SIGS = {
     "moe_combine": (ctypes.c_int, [_SP] + [_P] * 6),
     "moe_combine_bwd": (ctypes.c_int, [_SP] + [_P] * 10),
     "moe_unpermute_bwd": (ctypes.c_int, [_SP] + [_P] * 5),
+    "moe_route_bwd": (ctypes.c_int, [_SP] + [_P] * 9),
+    "moe_bias_update": (ctypes.c_int, [_SP, _P, ctypes.c_float, _P, _P]),
 }
 
 
@@ -247,6 +250,25 @@ def moe_unpermute_bwd(shape, dx_perm, pos, seg_offsets, dx, stream=None):
     _check("moe_unpermute_bwd", lib.moe_unpermute_bwd(
         ctypes.byref(shape), _ptr(dx_perm, "dx_perm", _bf16()), _ptr(pos, "pos", _i32()),
         _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(dx, "dx", _bf16()), st))
+
+
+def moe_route_bwd(shape, dtopk_w, topk_idx, probs, x, w_gate, dlogits, dw_gate, dx_router,
+                  stream=None):
+    lib = load_library()
+    st = _stream(stream, dlogits, dw_gate)
+    _check("moe_route_bwd", lib.moe_route_bwd(
+        ctypes.byref(shape), _ptr(dtopk_w, "dtopk_w", _f32()), _ptr(topk_idx, "topk_idx", _i32()),
+        _ptr(probs, "probs", _f32()), _ptr(x, "x", _bf16()), _ptr(w_gate, "w_gate", _f32()),
+        _ptr(dlogits, "dlogits", _f32()), _ptr(dw_gate, "dw_gate", _f32()),
+        _ptr(dx_router, "dx_router", _f32()), st))
+
+
+def moe_bias_update(shape, expert_counts, gamma, sel_bias, stream=None):
+    lib = load_library()
+    st = _stream(stream, sel_bias)
+    _check("moe_bias_update", lib.moe_bias_update(
+        ctypes.byref(shape), _ptr(expert_counts, "expert_counts", _i32()), float(gamma),
+        _ptr(sel_bias, "sel_bias", _f32()), st))
 
 
 # ------------------------------------------------------------------------------------------------

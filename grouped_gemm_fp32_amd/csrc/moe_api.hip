@@ -88,7 +88,7 @@ int64_t capacity(const moe_shape_t* s) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 const char* moe_status_string(int32_t status) {
   switch (status) {
@@ -300,6 +300,38 @@ moe_status_t moe_unpermute_bwd(const moe_shape_t* s, const uint16_t* dx_perm, co
   return hip_status(moe::launch_unpermute_bwd(*s, dx_perm, pos, seg_offsets, dx,
                                               (hipStream_t)stream),
                     "moe_unpermute_bwd");
+}
+
+moe_status_t moe_route_bwd(const moe_shape_t* s, const float* dtopk_w, const int32_t* topk_idx,
+                           const float* probs, const uint16_t* x, const float* w_gate,
+                           float* dlogits, float* dw_gate, float* dx_router, void* stream) {
+  CHECK_SHAPE(s);
+  if (s->T > 0) {
+    REQUIRE(dtopk_w);
+    REQUIRE(topk_idx);
+    REQUIRE(probs);
+    REQUIRE(dlogits);
+    if (dw_gate) REQUIRE(x);
+    if (dx_router) REQUIRE(w_gate);
+  }
+  if (s->T == 0 && !dw_gate) return MOE_OK;
+  return hip_status(moe::launch_route_bwd(*s, dtopk_w, topk_idx, probs, x, w_gate, dlogits, dw_gate,
+                                          dx_router, (hipStream_t)stream),
+                    "moe_route_bwd");
+}
+
+moe_status_t moe_bias_update(const moe_shape_t* s, const int32_t* expert_counts, float gamma,
+                             float* sel_bias, void* stream) {
+  CHECK_SHAPE(s);
+  REQUIRE(expert_counts);
+  REQUIRE(sel_bias);
+  if (!(gamma >= 0.0f) || gamma > 3.0e38f) {
+    set_err("gamma must be a finite number >= 0");
+    return MOE_ERR_INVALID_ARG;
+  }
+  return hip_status(moe::launch_bias_update(*s, expert_counts, gamma, sel_bias,
+                                            (hipStream_t)stream),
+                    "moe_bias_update");
 }
 
 }  // extern "C"

@@ -54,4 +54,11 @@ hipError_t launch_combine_bwd(const moe_shape_t& s, int64_t mcap, const uint16_t
 hipError_t launch_unpermute_bwd(const moe_shape_t& s, const uint16_t* dx_perm, const int32_t* pos,
                                 const int32_t* seg_offsets, uint16_t* dx, hipStream_t st);
 
+hipError_t launch_route_bwd(const moe_shape_t& s, const float* dtopk_w, const int32_t* topk_idx,
+                            const float* probs, const uint16_t* x, const float* wg, float* dlogits,
+                            float* dw_gate, float* dx_router, hipStream_t st);
+
+hipError_t launch_bias_update(const moe_shape_t& s, const int32_t* counts, float gamma, float* bias,
+                              hipStream_t st);
+
 }  // namespace moe

@@ -187,11 +187,46 @@ moe_status_t moe_combine_bwd(const moe_shape_t* shape, const uint16_t* dy, const
 
 /*
  * moe_unpermute_bwd — dx[t] = bf16( sum_j dx_perm[pos[t,j]] + sum_s dx_perm[seg_offsets[E+s]+t] )
- * (the expert path's part of the input gradient; the router's part is not computed here).
+ * (the expert path's part of the input gradient; moe_route_bwd gives the router's part).
  */
 moe_status_t moe_unpermute_bwd(const moe_shape_t* shape, const uint16_t* dx_perm,
                                const int32_t* pos, const int32_t* seg_offsets, uint16_t* dx,
                                void* stream);
+
+/*
+ * moe_route_bwd — the router's backward (TR section A2, load-balancing paragraph: the bias only
+ * selects; the routing weights come from the affinity scores). Given dtopk_w[T,K] = dL/dtopk_w
+ * (moe_combine_bwd's output) and the forward's topk_idx and probs:
+ *   MOE_NORM_TOPK: w_j = p_{e_j} / S (S summed in slot order, as moe_route does),
+ *                  c = sum_j w_j dtopk_w[t,j], dlogits[t,e_j] = w_j (dtopk_w[t,j] - c), and 0 on
+ *                  every unselected expert;
+ *   otherwise:     c = sum_j p_{e_j} dtopk_w[t,j], dlogits[t,e] = p_e (g_e - c) with
+ *                  g_{e_j} = dtopk_w[t,j] and g = 0 elsewhere.
+ * The selection (piecewise constant) passes no gradient and sel_bias gets none.
+ *   dw_gate[E,H]   = dlogits^T x          (fp32; optional, needs x)
+ *   dx_router[T,H] = dlogits w_gate       (fp32; the router's share of the input gradient,
+ *                                          to be added to moe_unpermute_bwd's; optional, needs w_gate)
+ * Layouts: dtopk_w, topk_idx [T,K]; probs, dlogits [T,E] fp32; x [T,H] bf16; w_gate [E,H] fp32.
+ * Required when T > 0: dtopk_w, topk_idx, probs, dlogits. With T == 0 nothing is read and dw_gate
+ * (if given) is filled with zeros. Logit_bias, if the forward used one, gets sum_t dlogits[t,e]; it
+ * is not computed here.
+ */
+moe_status_t moe_route_bwd(const moe_shape_t* shape, const float* dtopk_w, const int32_t* topk_idx,
+                           const float* probs, const uint16_t* x, const float* w_gate,
+                           float* dlogits, float* dw_gate, float* dx_router, void* stream);
+
+/*
+ * moe_bias_update — one step of the aux-loss-free load balancing (TR section A2, load-balancing
+ * paragraph: the per-expert bias is adjusted during training to keep the loads balanced; the
+ * rule is a reading): with the mean load T*K/E,
+ *   sel_bias[e] += gamma  if expert_counts[e] < T*K/E,
+ *   sel_bias[e] -= gamma  if expert_counts[e] > T*K/E, unchanged if equal
+ * (the comparison is exact in integers; the update one fp32 add). sel_bias [E] fp32 is updated in
+ * place; expert_counts [E] int32 is moe_route's output. gamma (the update speed) must be a
+ * finite number >= 0, else MOE_ERR_INVALID_ARG.
+ */
+moe_status_t moe_bias_update(const moe_shape_t* shape, const int32_t* expert_counts, float gamma,
+                             float* sel_bias, void* stream);
 
 #ifdef __cplusplus
 }

@@ -109,6 +109,25 @@ def test_null_required_pointers(lib):
     assert "NULL" in M.moe_last_error()
 
 
+def test_router_backward_and_bias_update_checks(lib):
+    s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
+    d = ctypes.c_void_p(16)
+    # required: dtopk_w, topk_idx, probs, dlogits; dw_gate needs x, dx_router needs w_gate
+    for i in range(4):
+        a = [d, d, d, None, None, d, None, None]
+        a[[0, 1, 2, 5][i]] = None
+        assert lib.moe_route_bwd(ctypes.byref(s), *a, None) == -1, i
+    assert lib.moe_route_bwd(ctypes.byref(s), d, d, d, None, d, d, d, None, None) == -1  # dw_gate, no x
+    assert lib.moe_route_bwd(ctypes.byref(s), d, d, d, d, None, d, None, d, None) == -1  # dx, no w_gate
+    s0 = M.make_shape(0, 256, 8, 2, 128, 1, 16)
+    assert lib.moe_route_bwd(ctypes.byref(s0), *([None] * 8), None) == 0
+    assert lib.moe_bias_update(ctypes.byref(s), None, 0.001, d, None) == -1
+    assert lib.moe_bias_update(ctypes.byref(s), d, 0.001, None, None) == -1
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert lib.moe_bias_update(ctypes.byref(s), d, bad, d, None) == -1
+        assert "gamma" in M.moe_last_error()
+
+
 def test_gemm_tensors_must_be_16_byte_aligned(lib):
     s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
     d, odd = ctypes.c_void_p(16), ctypes.c_void_p(16 + 8)
