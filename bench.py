@@ -18,7 +18,9 @@ random routing, 2 shared experts, block 16).
 
 Prints one JSON line. `value` is the useful grouped-GEMM TFLOP/s of the whole step (padding
 excluded). It also carries the dominant kernel's roofline, timed with HIP events on the launch
-stream, and the CPU oracle's throughput on a bounded sample of the same workload.
+stream, and the CPU oracle's throughput on a bounded sample of the same workload. With the default
+workload it also times, outside the step, the router backward on the step's routing (dlogits, then
+dWg and the router's share of dx in fp32) and the load-balancing bias update.
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "grouped-GEMM bf16 TFLOP/s (% MFMA peak) and MoE-layer tokens/s, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 (matrix and vector)
 
 
 def log(msg):
@@ -125,6 +128,41 @@ def _time_steps(torch, np, step, nstages, steps, warmup):
     stage_ms = [float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in events]))
                 for i in range(nstages)]
     return wall * 1e3 / steps, stage_ms
+
+
+def _time_call(torch, np, fn, reps):
+    """Mean HIP-event time (ms) of fn() on the current stream, after one untimed call."""
+    fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for k in range(reps):
+        ev[k].record()
+        fn()
+    ev[reps].record()
+    torch.cuda.synchronize()
+    return float(np.mean([ev[k].elapsed_time(ev[k + 1]) for k in range(reps)]))
+
+
+def router_backward_timing(torch, np, M, Sy, cfg, s, b, X, dev, reps=20):
+    """The router backward on the step's own routing and weight gradients (not part of the step):
+    dlogits alone, then with dWg = dlogits^T x and dx_router = dlogits Wg; and the bias update."""
+    T, H, E = cfg.T, cfg.H, cfg.E
+    WG = torch.from_numpy(Sy.draw_wg(cfg)).to(dev)
+    dz = torch.empty(T, E, device=dev)
+    dwg = torch.empty(E, H, device=dev)
+    dxr = torch.empty(T, H, device=dev)
+    sb = torch.zeros(E, device=dev)
+    args = (s, b["dtopk_w"], b["topk_idx"], b["probs"], X, WG, dz)
+    t_dz = _time_call(torch, np, lambda: M.moe_route_bwd(*args, None, None), reps)
+    t_dwg = _time_call(torch, np, lambda: M.moe_route_bwd(*args, dwg, None), reps) - t_dz
+    t_dx = _time_call(torch, np, lambda: M.moe_route_bwd(*args, None, dxr), reps) - t_dz
+    t_all = _time_call(torch, np, lambda: M.moe_route_bwd(*args, dwg, dxr), reps)
+    t_bias = _time_call(torch, np, lambda: M.moe_bias_update(s, b["expert_counts"], 1e-3, sb), reps)
+    flops = 2.0 * T * E * H                # each of dWg and dx_router, fp32
+    return {"ms": round(t_all, 4), "dlogits_ms": round(t_dz, 4),
+            "dwg_ms": round(t_dwg, 4), "dwg_tflops": round(flops / (t_dwg * 1e-3) / 1e12, 2),
+            "dx_ms": round(t_dx, 4), "dx_tflops": round(flops / (t_dx * 1e-3) / 1e12, 2),
+            "fp32_peak_tflops": PEAK_FP32_TFLOPS, "bias_update_ms": round(t_bias, 4)}
 
 
 def main():
@@ -235,6 +273,7 @@ def main():
         assert np.all(counts == T * K // E), "uniform routing not reproduced"
     ms_step, st_ms = _time_steps(torch, np, step, len(stages), args.steps, args.warmup)
     stage_ms = dict(zip(stages, st_ms))
+    router_bwd = (router_backward_timing(torch, np, M, Sy, cfg, s, b, X, dev) if fwd_bwd else None)
 
     rows = T * K + S * T                       # useful rows (padding excluded)
     per_row = {"fwd_gateup": 4.0 * H * I, "fwd_down": 2.0 * H * I}
@@ -289,6 +328,8 @@ def main():
                           for k in per_row},
         "experts_touched": touched,
     }
+    if router_bwd is not None:
+        out["router_backward"] = router_bwd
     sample = args.cpu_sample if args.cpu_sample is not None else {"c2": 384, "c3": 256,
                                                                    "c5": 256}[args.workload]
     if sample > 0:

@@ -311,7 +311,7 @@ moe_status_t moe_route_bwd(const moe_shape_t* s, const float* dtopk_w, const int
     REQUIRE(topk_idx);
     REQUIRE(probs);
     REQUIRE(dlogits);
-    if (dw_gate) REQUIRE(x);
+    if (dw_gate) REQUIRE_T(x);
     if (dx_router) REQUIRE(w_gate);
   }
   if (s->T == 0 && !dw_gate) return MOE_OK;

@@ -13,11 +13,11 @@
 //                       and 0 elsewhere; unnormalised weights: c = sum_k p_k dw_k and
 //                       dlogits_e = p_e (g_e - c) with g_e = dw_k on the selected experts.
 //   router_dwg_kernel   dWg[E,H] = dlogits^T x, an fp32 contraction over the tokens on the fp32
-//                       matrix unit (v_mfma_f32_32x32x2_f32): one workgroup per 32 x 32 tile of dWg,
-//                       its four wavefronts take a quarter of the tokens each and their partial
+//                       matrix unit (v_mfma_f32_32x32x2_f32): one workgroup per 32 x 64 tile of dWg,
+//                       its eight wavefronts take an eighth of the tokens each and their partial
 //                       sums are added in wavefront order (deterministic).
 //   router_dx_kernel    dx_router[T,H] = dlogits Wg, the same instruction with the contraction
-//                       over the experts: a 32-token tile of dlogits in LDS, Wg read from L2.
+//                       over the experts: a 64-token tile of dlogits in LDS, Wg read from L2.
 //   bias_update_kernel  b_e += gamma * sign(T K - E c_e), one fp32 add per expert.
 #include "moe_common.h"
 #include "moe_internal.h"
@@ -27,7 +27,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 2048;   // target wavefront count of the per-token kernel
-constexpr int kMaxE = 256;     // most routed experts a shape may have
 
 // ---- dlogits ------------------------------------------------------------------------------------
 template <bool NORM>
@@ -82,83 +81,129 @@ __global__ __launch_bounds__(kThreads) void route_bwd_kernel(int T, int E, int K
 // MFMA 32x32x2 f32: lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the result D[i][j]
 // sits in lane j (+32 for rows 4..7 of each group of 8), register q -> row 8 (q / 4) + 4 (l / 32)
 // + q % 4.
-constexpr int kDwgUnroll = 8;
+// A workgroup of eight wavefronts covers a 32 x 64 tile of dWg; each wavefront takes an eighth of
+// the tokens for the whole tile, as two MFMA blocks (even and odd columns) that share each dlogits
+// operand, so every lane loads one fp32 and one bf16 pair per two MFMAs. The partial sums are
+// added in wavefront order (deterministic).
+constexpr int kDwgThreads = 512;
+constexpr int kDwgUnroll = 16;  // token pairs per batch; the next batch's operands load during it
 
-__global__ __launch_bounds__(kThreads) void router_dwg_kernel(int T, int H, int E,
-                                                              const float* __restrict__ dz,
-                                                              const uint16_t* __restrict__ x,
-                                                              float* __restrict__ dwg) {
-  __shared__ float red[4][32][33];
+__global__ __launch_bounds__(kDwgThreads) void router_dwg_kernel(int T, int H, int E,
+                                                                 const float* __restrict__ dz,
+                                                                 const uint16_t* __restrict__ x,
+                                                                 float* __restrict__ dwg) {
+  __shared__ float red[8][32][65];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e0 = blockIdx.x * 32, h0 = blockIdx.y * 32;
+  const int e0 = blockIdx.x * 32, h0 = blockIdx.y * 64;
   const int r = lane & 31, kh = lane >> 5;
-  const int e = e0 + r, h = h0 + r;
+  const int e = e0 + r;
   const bool e_ok = e < E;
-  // this wave's quarter of the tokens, in pairs (one MFMA each)
-  const int per = (((T + 3) / 4) + 1) & ~1;
+  // this wave's eighth of the tokens, in pairs (one k-step of the MFMA each)
+  const int per = (((T + 7) / 8) + 1) & ~1;
   const int ta = min(T, wave * per), tz = min(T, ta + per);
-  f32x16_t acc;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
-  for (int t0 = ta; t0 < tz; t0 += 2 * kDwgUnroll) {
-    float a[kDwgUnroll], b[kDwgUnroll];
+  const uint32_t* x2 = reinterpret_cast<const uint32_t*>(x);   // H is even: pairs never straddle rows
+  auto load = [&](int t0, float (&a)[kDwgUnroll], uint32_t (&b)[kDwgUnroll]) {
 #pragma unroll
     for (int u = 0; u < kDwgUnroll; ++u) {
       const int t = t0 + 2 * u + kh;
       const bool ok = t < tz;
       a[u] = (ok && e_ok) ? dz[(int64_t)t * E + e] : 0.0f;
-      b[u] = ok ? __uint_as_float((uint32_t)x[(int64_t)t * H + h] << 16) : 0.0f;
+      b[u] = ok ? x2[((int64_t)t * H + h0) / 2 + r] : 0u;
+    }
+  };
+  f32x16_t acc0, acc1;   // columns h0 + 2 r and h0 + 2 r + 1
+#pragma unroll
+  for (int q = 0; q < 16; ++q) { acc0[q] = 0.0f; acc1[q] = 0.0f; }
+  float a[kDwgUnroll];
+  uint32_t b[kDwgUnroll];
+  load(ta, a, b);
+  for (int t0 = ta; t0 < tz; t0 += 2 * kDwgUnroll) {
+    float an[kDwgUnroll];
+    uint32_t bn[kDwgUnroll];
+    load(t0 + 2 * kDwgUnroll, an, bn);   // past tz: zeros, no memory access
+#pragma unroll
+    for (int u = 0; u < kDwgUnroll; ++u) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], __uint_as_float(b[u] << 16), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], __uint_as_float(b[u] & 0xffff0000u), acc1,
+                                                  0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < kDwgUnroll; ++u)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], acc, 0, 0, 0);
+    for (int u = 0; u < kDwgUnroll; ++u) { a[u] = an[u]; b[u] = bn[u]; }
   }
-  // D[e][h]: lane -> h = h0 + r, register q -> e = e0 + 8 (q / 4) + 4 kh + q % 4
+  // D[e][h]: lane -> column r of the block, register q -> e = e0 + 8 (q / 4) + 4 kh + q % 4
 #pragma unroll
-  for (int q = 0; q < 16; ++q) red[wave][8 * (q >> 2) + 4 * kh + (q & 3)][r] = acc[q];
+  for (int q = 0; q < 16; ++q) {
+    const int el = 8 * (q >> 2) + 4 * kh + (q & 3);
+    red[wave][el][2 * r] = acc0[q];
+    red[wave][el][2 * r + 1] = acc1[q];
+  }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 32 * 32; idx += kThreads) {
-    const int el = idx / 32, hl = idx % 32;
+  for (int idx = threadIdx.x; idx < 32 * 64; idx += kDwgThreads) {
+    const int el = idx / 64, hl = idx % 64;
     if (e0 + el < E) {
-      const float v = red[0][el][hl] + red[1][el][hl] + red[2][el][hl] + red[3][el][hl];
+      float v = red[0][el][hl];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) v += red[w][el][hl];
       dwg[(int64_t)(e0 + el) * H + h0 + hl] = v;
     }
   }
 }
 
 // ---- dx_router = dlogits Wg ---------------------------------------------------------------------
-constexpr int kDxTok = 32;
+// A workgroup covers 64 tokens x 128 columns; each wavefront 64 tokens x 32 columns (two MFMA
+// blocks sharing every Wg operand), with the Wg loads of the next batch of experts in flight.
+constexpr int kDxTok = 64;
+constexpr int kDxUnroll = 16;  // expert pairs per batch
 
 __global__ __launch_bounds__(kThreads) void router_dx_kernel(int T, int H, int E,
                                                              const float* __restrict__ dz,
                                                              const float* __restrict__ wg,
                                                              float* __restrict__ dx) {
-  __shared__ float tile[kDxTok * (kMaxE + 1)];
+  extern __shared__ float tile[];   // [kDxTok][E + 1], sized at launch
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kDxTok, h0 = blockIdx.y * 128 + wave * 32;
   const int nt = min(kDxTok, T - t0);
   const int ld = E + 1;
-  for (int i = threadIdx.x; i < kDxTok * E; i += kThreads) {
-    const int tl = i / E, e = i % E;
-    tile[tl * ld + e] = tl < nt ? dz[(int64_t)(t0 + tl) * E + e] : 0.0f;
-  }
+  // wavefront w fills rows w, w + 4, ...; a row's experts go across the lanes (coalesced)
+#pragma unroll 4
+  for (int tl = wave; tl < kDxTok; tl += kThreads / 64)
+    for (int e = lane; e < E; e += 64)
+      tile[tl * ld + e] = tl < nt ? dz[(int64_t)(t0 + tl) * E + e] : 0.0f;
   __syncthreads();
   const int r = lane & 31, kh = lane >> 5;
-  f32x16_t acc;
+  auto load = [&](int e0, float (&b)[kDxUnroll]) {
 #pragma unroll
-  for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+    for (int u = 0; u < kDxUnroll; ++u) {
+      const int e = e0 + 2 * u + kh;
+      b[u] = e < E ? wg[(int64_t)e * H + h0 + r] : 0.0f;
+    }
+  };
+  f32x16_t acc0, acc1;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) { acc0[q] = 0.0f; acc1[q] = 0.0f; }
   // D[t][h] = sum_e A[t][e] B[e][h]: A from the LDS tile, B = Wg rows (128 contiguous bytes)
-  for (int e0 = 0; e0 < E; e0 += 2) {
-    const int e = e0 + kh;
-    const float a = e < E ? tile[r * ld + e] : 0.0f;
-    const float b = e < E ? wg[(int64_t)e * H + h0 + r] : 0.0f;
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+  float b[kDxUnroll];
+  load(0, b);
+  for (int e0 = 0; e0 < E; e0 += 2 * kDxUnroll) {
+    float bn[kDxUnroll];
+    load(e0 + 2 * kDxUnroll, bn);   // past E: zeros, no memory access
+#pragma unroll
+    for (int u = 0; u < kDxUnroll; ++u) {
+      const int e = e0 + 2 * u + kh;
+      const float a0 = e < E ? tile[r * ld + e] : 0.0f;
+      const float a1 = e < E ? tile[(32 + r) * ld + e] : 0.0f;
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b[u], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b[u], acc1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kDxUnroll; ++u) b[u] = bn[u];
   }
-  // lane -> h = h0 + r, register q -> t = t0 + 8 (q / 4) + 4 kh + q % 4
+  // lane -> h = h0 + r, register q -> t = t0 + 8 (q / 4) + 4 kh + q % 4 (+32 for the second block)
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int tl = 8 * (q >> 2) + 4 * kh + (q & 3);
-    if (tl < nt) dx[(int64_t)(t0 + tl) * H + h0 + r] = acc[q];
+    if (tl < nt) dx[(int64_t)(t0 + tl) * H + h0 + r] = acc0[q];
+    if (tl + 32 < nt) dx[(int64_t)(t0 + tl + 32) * H + h0 + r] = acc1[q];
   }
 }
 
@@ -203,14 +248,20 @@ hipError_t launch_route_bwd(const moe_shape_t& s, const float* dtopk_w, const in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dw_gate) {
-    hipLaunchKernelGGL(router_dwg_kernel, dim3((unsigned)((s.E + 31) / 32), (unsigned)(s.H / 32)),
-                       dim3(kThreads), 0, st, s.T, s.H, s.E, dlogits, x, dw_gate);
+    hipLaunchKernelGGL(router_dwg_kernel, dim3((unsigned)((s.E + 31) / 32), (unsigned)(s.H / 64)),
+                       dim3(kDwgThreads), 0, st, s.T, s.H, s.E, dlogits, x, dw_gate);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (dx_router) {
+    const size_t lds = sizeof(float) * kDxTok * (s.E + 1);   // at most 64 KiB + 256 B (E <= 256)
+    if (lds > 65536) {
+      e = hipFuncSetAttribute((const void*)router_dx_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(router_dx_kernel, dim3((unsigned)((s.T + kDxTok - 1) / kDxTok), (unsigned)(s.H / 128)),
-                       dim3(kThreads), 0, st, s.T, s.H, s.E, dlogits, wg, dx_router);
+                       dim3(kThreads), lds, st, s.T, s.H, s.E, dlogits, wg, dx_router);
     e = hipGetLastError();
   }
   return e;

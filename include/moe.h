@@ -207,7 +207,8 @@ moe_status_t moe_unpermute_bwd(const moe_shape_t* shape, const uint16_t* dx_perm
  *   dx_router[T,H] = dlogits w_gate       (fp32; the router's share of the input gradient,
  *                                          to be added to moe_unpermute_bwd's; optional, needs w_gate)
  * Layouts: dtopk_w, topk_idx [T,K]; probs, dlogits [T,E] fp32; x [T,H] bf16; w_gate [E,H] fp32.
- * Required when T > 0: dtopk_w, topk_idx, probs, dlogits. With T == 0 nothing is read and dw_gate
+ * Required when T > 0: dtopk_w, topk_idx, probs, dlogits; x 16-byte aligned when dw_gate is
+ * given (else MOE_ERR_INVALID_ARG). With T == 0 nothing is read and dw_gate
  * (if given) is filled with zeros. Logit_bias, if the forward used one, gets sum_t dlogits[t,e]; it
  * is not computed here.
  */
