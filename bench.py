@@ -14,7 +14,8 @@ assignment, so the selection kernel runs but decides nothing else.
 
 Other workloads (forward only, routing computed from x): `--workload c3` is the skewed full layer
 (T=16384, Zipf logit offsets, 2 shared experts, block 128); `--workload c5` is decode (T=256,
-random routing, 2 shared experts, block 16).
+random routing, 2 shared experts, block 16). `--workload dense` runs the default step on a dense
+SwiGLU FFN expressed as one group (E = K = 1, intermediate 11264).
 
 Prints one JSON line. `value` is the useful grouped-GEMM TFLOP/s of the whole step (padding
 excluded). It also carries the dominant kernel's roofline, timed with HIP events on the launch
@@ -170,9 +171,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("c2", "c3", "c5"), default="c2",
+    ap.add_argument("--workload", choices=("c2", "c3", "c5", "dense"), default="c2",
                     help="c2: forward+backward at the uniform 8192-token shape (default); c3: skewed "
-                         "16384-token full layer forward; c5: 256-token decode forward")
+                         "16384-token full layer forward; c5: 256-token decode forward; dense: "
+                         "forward+backward of a dense SwiGLU FFN (intermediate 11264) as one group")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, copy a cold buffer of this many MiB (a plain copy of known "
                          "size that scales the HBM byte counters)")
@@ -198,7 +200,7 @@ def main():
     log(f"[bench] {args.workload}: generating inputs T={T} H={H} E={E} K={K} I={I} S={S} B={B}")
     t0 = time.perf_counter()
     x, w1, w2 = Sy.draw_x(cfg), Sy.draw_w1_all(cfg), Sy.draw_w2_all(cfg)
-    fwd_bwd = args.workload == "c2"
+    fwd_bwd = args.workload in ("c2", "dense")
     if fwd_bwd:
         dy, logits = Sy.draw_dy(cfg), Sy.uniform_logits(cfg)
     else:
@@ -273,7 +275,8 @@ def main():
         assert np.all(counts == T * K // E), "uniform routing not reproduced"
     ms_step, st_ms = _time_steps(torch, np, step, len(stages), args.steps, args.warmup)
     stage_ms = dict(zip(stages, st_ms))
-    router_bwd = (router_backward_timing(torch, np, M, Sy, cfg, s, b, X, dev) if fwd_bwd else None)
+    router_bwd = (router_backward_timing(torch, np, M, Sy, cfg, s, b, X, dev)
+                  if args.workload == "c2" else None)
 
     rows = T * K + S * T                       # useful rows (padding excluded)
     per_row = {"fwd_gateup": 4.0 * H * I, "fwd_down": 2.0 * H * I}
@@ -306,7 +309,9 @@ def main():
                                     if traffic is not None else None),
                     "per_unit": f"{per_row[dom]:.0f} FLOP per useful row x {rows} rows per launch",
                     "avg_launch_ms": round(stage_ms[dom], 4)}
-    desc = {"c2": "grouped-GEMM MoE FFN forward+backward, uniform routing (T=8192, hidden=4096, "
+    desc = {"dense": "dense SwiGLU FFN as one group, forward+backward (T=8192, hidden=4096, "
+                     "intermediate=11264, block_m=128)",
+            "c2": "grouped-GEMM MoE FFN forward+backward, uniform routing (T=8192, hidden=4096, "
                   "128 experts top-6, intermediate=1408, block_m=128, 384 rows per expert)",
             "c3": "MoE FFN full layer forward from x, skewed routing (T=16384, hidden=4096, 128 "
                   "experts top-6 with Zipf(1.1) logit offsets + 2 shared experts, intermediate=1408, "
@@ -330,7 +335,17 @@ def main():
     }
     if router_bwd is not None:
         out["router_backward"] = router_bwd
-    sample = args.cpu_sample if args.cpu_sample is not None else {"c2": 384, "c3": 256,
+    if args.workload == "dense":
+        # Context only: the same gate/up product as one plain library GEMM (torch.mm, which ROCm
+        # serves with hipBLASLt), on the same operands, outside the step.
+        W1t = W1.view(2 * I, H).t().contiguous()
+        t_lib = _time_call(torch, np, lambda: torch.mm(X, W1t), 20)
+        out["library_gemm_ref"] = {
+            "what": "torch.mm of x [T,H] by W1^T [H,2I] in bf16 (the gate/up forward GEMM)",
+            "ms": round(t_lib, 4), "tflops": round(4.0 * T * H * I / (t_lib * 1e-3) / 1e12, 1),
+            "this_library_fwd_gateup_ms": round(stage_ms["fwd_gateup"], 4)}
+        del W1t
+    sample = args.cpu_sample if args.cpu_sample is not None else {"c2": 384, "c3": 256, "dense": 8192,
                                                                    "c5": 256}[args.workload]
     if sample > 0:
         log(f"[bench] CPU oracle on {sample} tokens")

@@ -73,6 +73,10 @@ CONFIGS = {
     # Decode-sized sparse layer.
     "c5": MoEConfig("c5", T=256, H=4096, E=128, K=6, I=1408, S=2, block_m=16, seed=7,
                     routing="router"),
+    # A dense SwiGLU FFN (the model's first layer) run as one group: E = K = 1. The pages do not give
+    # its width; the reading is the active experts' total width per token, 8 x 1408 = 11264.
+    "dense": MoEConfig("dense", T=8192, H=4096, E=1, K=1, I=11264, S=0, block_m=128, seed=0,
+                       routing="uniform"),
     # Decode with 16 experts forced empty by a -10 selection bias (empty-group skipping).
     "c5e": MoEConfig("c5e", T=256, H=4096, E=128, K=6, I=1408, S=2, block_m=16, seed=7,
                      routing="router", sel_bias="forced_empty",

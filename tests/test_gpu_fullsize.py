@@ -165,6 +165,50 @@ def test_uniform_8192_tokens_forward_and_backward():
         assert_bf16_close(vals_host(buf["dw2"][g]), dw2[0], f"dw2[{g}]")
 
 
+def test_dense_ffn_8192_tokens_forward_and_backward():
+    """Dense SwiGLU FFN as one group (E = K = 1): T=8192, hidden 4096, intermediate 11264, block 128.
+
+    With one expert of weight 1 the combine and the unpermute are exact copies (y = y_perm, dx =
+    dx_perm, dy_perm = dy, bit for bit); sampled rows are checked through the FFN and its dgrad.
+    """
+    cfg = get_config("dense")
+    log(f"full size: {cfg}")
+    s = M.make_shape(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.S, cfg.block_m)
+    x, dy, logits = draw_x(cfg), draw_dy(cfg), uniform_logits(cfg)
+    w1, w2 = draw_w1_all(cfg), draw_w2_all(cfg)
+    X, W1, W2 = bf16_dev(x), bf16_dev(w1), bf16_dev(w2)
+    buf = _run_forward(cfg, s, X, W1, W2, dict(x=None, w_gate=None, logit_bias=None, sel_bias=None,
+                                               logits=f32_dev(logits)))
+    idx = np.zeros((cfg.T, 1), np.int32)
+    np.testing.assert_array_equal(_np(buf["topk_idx"]), idx)
+    assert np.all(_np(buf["topk_w"]) == 1.0)
+    seg, rt, pos, total = _check_maps_exact(buf, idx, cfg)
+    assert total == cfg.T and np.array_equal(rt[:total], np.arange(cfg.T))
+    np.testing.assert_array_equal(bits_host(buf["x_perm"][:total]), x)
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 1, 383, 384, cfg.T - 1], rng.integers(0, cfg.T, 27)]))
+    h_ref, a_ref, y_ref = _oracle_rows(rows, seg, rt, x, cfg, lambda g: w1[g], lambda g: w2[g])
+    R = torch.from_numpy(rows).to(DEV)
+    assert_bf16_close(vals_host(buf["h_save"][R]), O.round_bf16(h_ref), "h_save rows")
+    assert_bf16_close(vals_host(buf["a"][R]), a_ref, "a rows")
+    assert_bf16_close(vals_host(buf["y_perm"][R]), y_ref, "y_perm rows")
+    assert torch.equal(buf["y"].view(torch.int16), buf["y_perm"][:cfg.T].view(torch.int16))
+    DY = bf16_dev(dy)
+    M.moe_combine_bwd(s, DY, buf["y_perm"], buf["pos"], buf["topk_w"], buf["seg_offsets"],
+                      buf["row_token"], buf["total_rows"], buf["dy_perm"], buf["dtopk_w"])
+    M.grouped_gemm_bwd(s, M.MOE_DGRAD | M.MOE_WGRAD, buf["x_perm"], buf["h_save"], buf["a"],
+                       buf["dy_perm"], buf["seg_offsets"], buf["tile_group"], buf["total_rows"],
+                       W1, W2, buf["dh"], buf["dx_perm"], buf["dw1"], buf["dw2"])
+    M.moe_unpermute_bwd(s, buf["dx_perm"], buf["pos"], buf["seg_offsets"], buf["dx"])
+    torch.cuda.synchronize()
+    assert torch.equal(buf["dy_perm"][:cfg.T].view(torch.int16), DY.view(torch.int16))
+    assert torch.equal(buf["dx"].view(torch.int16), buf["dx_perm"][:cfg.T].view(torch.int16))
+    dh_ref, dx_ref = O.expert_ffn_dgrad(O.bf16_to_f64(dy[rows]), O.round_bf16(h_ref),
+                                        [0, len(rows)], [w1[0]], [w2[0]], cfg.I)
+    assert_bf16_close(vals_host(buf["dh"][R]), dh_ref, "dh rows")
+    assert_bf16_close(vals_host(buf["dx_perm"][R]), dx_ref, "dx_perm rows")
+
+
 def test_skewed_16384_tokens_full_layer():
     """Router with Zipf(1.1) logit offsets, two shared experts, block 128; forward."""
     cfg = get_config("c3")

@@ -237,6 +237,9 @@ def _compare_layer(buf, f, b):
     # from empty to 24 contraction stages: tiles chained and not chained within one workgroup
     (1500, 1024, 64, 4, 256, 1, 64, (3, 17, 40)),
     (1500, 1024, 64, 4, 256, 1, 128, (5,)),
+    # a dense SwiGLU FFN as one group (E = K = 1): one segment of every token, many row tiles
+    (1000, 512, 1, 1, 1024, 0, 128, ()),
+    (777, 256, 1, 1, 320, 0, 64, ()),
 ])
 def test_layer_parity(T, H, E, K, I, S, B, empty):
     log(f"layer T={T} H={H} E={E} K={K} I={I} S={S} B={B} empty={empty}")
