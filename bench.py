@@ -335,6 +335,18 @@ def main():
     }
     if router_bwd is not None:
         out["router_backward"] = router_bwd
+    if args.workload == "c2":
+        # Context only: the gate/up product as a plain batched library GEMM (torch.bmm, served by
+        # hipBLASLt) over the 128 experts' 384-row segments, operands made contiguous first.
+        Xb = b["x_perm"][:T * K].view(E, T * K // E, H)
+        W1t = W1.view(E, 2 * I, H).transpose(1, 2).contiguous()
+        t_lib = _time_call(torch, np, lambda: torch.bmm(Xb, W1t), 20)
+        out["library_gemm_ref"] = {
+            "what": "torch.bmm of the 128 segments [384,H] by W1_e^T [H,2I] in bf16 (the gate/up "
+                    "forward GEMM without the SwiGLU)",
+            "ms": round(t_lib, 4), "tflops": round(4.0 * T * K * H * I / (t_lib * 1e-3) / 1e12, 1),
+            "this_library_fwd_gateup_ms": round(stage_ms["fwd_gateup"], 4)}
+        del W1t
     if args.workload == "dense":
         # Context only: the same gate/up product as one plain library GEMM (torch.mm, which ROCm
         # serves with hipBLASLt), on the same operands, outside the step.
