@@ -17,7 +17,8 @@ __all__ = [
     "MOE_WGRAD",
     "moe_abi_version", "moe_status_string", "moe_last_error", "moe_row_capacity",
     "moe_workspace_size", "moe_route", "moe_permute", "grouped_gemm_fwd", "grouped_gemm_bwd",
-    "moe_combine", "moe_combine_bwd", "moe_unpermute_bwd", "moe_route_bwd", "moe_bias_update",
+    "grouped_gemm_wgrad_f32", "moe_combine", "moe_combine_bwd", "moe_unpermute_bwd",
+    "moe_route_bwd", "moe_bias_update",
     "make_shape", "alloc_buffers",
 ]
 
@@ -78,6 +79,7 @@ _SIGS = {
     "moe_combine_bwd": (ctypes.c_int, [_SP] + [_P] * 10),
     "moe_unpermute_bwd": (ctypes.c_int, [_SP] + [_P] * 5),
     "moe_route_bwd": (ctypes.c_int, [_SP] + [_P] * 9),
+    "grouped_gemm_wgrad_f32": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 8),
     "moe_bias_update": (ctypes.c_int, [_SP, _P, ctypes.c_float, _P, _P]),
 }
 
@@ -250,6 +252,17 @@ def moe_unpermute_bwd(shape, dx_perm, pos, seg_offsets, dx, stream=None):
     _check("moe_unpermute_bwd", lib.moe_unpermute_bwd(
         ctypes.byref(shape), _ptr(dx_perm, "dx_perm", _bf16()), _ptr(pos, "pos", _i32()),
         _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(dx, "dx", _bf16()), st))
+
+
+def grouped_gemm_wgrad_f32(shape, which, x_perm, a, dy_perm, dh, seg_offsets, dw1, dw2,
+                           stream=None):
+    lib = load_library()
+    st = _stream(stream, dw1, dw2)
+    _check("grouped_gemm_wgrad_f32", lib.grouped_gemm_wgrad_f32(
+        ctypes.byref(shape), int(which), _ptr(x_perm, "x_perm", _bf16()), _ptr(a, "a", _bf16()),
+        _ptr(dy_perm, "dy_perm", _bf16()), _ptr(dh, "dh", _bf16()),
+        _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(dw1, "dw1", _f32()),
+        _ptr(dw2, "dw2", _f32()), st))
 
 
 def moe_route_bwd(shape, dtopk_w, topk_idx, probs, x, w_gate, dlogits, dw_gate, dx_router,

@@ -244,10 +244,40 @@ moe_status_t grouped_gemm_bwd(const moe_shape_t* s, uint32_t which, const uint16
   }
   if (which & MOE_WGRAD) {
     return hip_status(moe::launch_ggemm_wgrad(*s, which, x_perm, a, dy_perm, dh, seg_offsets, dw1,
-                                              dw2, st),
+                                              dw2, false, st),
                       "grouped_gemm_bwd(wgrad)");
   }
   return MOE_OK;
+}
+
+moe_status_t grouped_gemm_wgrad_f32(const moe_shape_t* s, uint32_t which, const uint16_t* x_perm,
+                                    const uint16_t* a, const uint16_t* dy_perm, const uint16_t* dh,
+                                    const int32_t* seg_offsets, float* dw1, float* dw2,
+                                    void* stream) {
+  CHECK_SHAPE(s);
+  if (which == 0 || (which & ~(uint32_t)MOE_WGRAD)) {
+    set_err("which must be a non-empty combination of the MOE_WGRAD_* bits");
+    return MOE_ERR_INVALID_ARG;
+  }
+  const bool rows = s->T > 0;
+  REQUIRE(seg_offsets);
+  if (which & MOE_WGRAD_DOWN) {
+    REQUIRE_T(dw2);
+    if (rows) {
+      REQUIRE_T(dy_perm);
+      REQUIRE_T(a);
+    }
+  }
+  if (which & MOE_WGRAD_GATEUP) {
+    REQUIRE_T(dw1);
+    if (rows) {
+      REQUIRE_T(dh);
+      REQUIRE_T(x_perm);
+    }
+  }
+  return hip_status(moe::launch_ggemm_wgrad(*s, which, x_perm, a, dy_perm, dh, seg_offsets, dw1, dw2,
+                                            true, (hipStream_t)stream),
+                    "grouped_gemm_wgrad_f32");
 }
 
 moe_status_t moe_combine(const moe_shape_t* s, const uint16_t* y_perm, const int32_t* pos,

@@ -1213,38 +1213,61 @@ __global__ __launch_bounds__(kThreads, 1) void ggemm_block64_kernel(GemmArgs p) 
 typedef Tile8<256, 256, 4, 2> Wgrad8Tile;
 constexpr int kStoreNT = 2;   // cache-policy operand of buffer stores: non-temporal
 constexpr int kWgradScr = 4096;                     // epilogue staging per wavefront
-constexpr int kWgradStores = Wgrad8Tile::TM * (Wgrad8Tile::TN / 2) * 4;   // stores per wave per tile
+// Stores per wavefront per tile: bf16 dW in 32 x 64 passes (4 stores each); fp32 dW in 32 x 32
+// passes (4 stores each, twice as many passes).
+template <bool F32> constexpr int wgrad_stores() {
+  return Wgrad8Tile::TM * (F32 ? Wgrad8Tile::TN : Wgrad8Tile::TN / 2) * 4;
+}
 static_assert(2 * Wgrad8Tile::STAGE + Wgrad8Tile::NW * kWgradScr <= kLdsBytes, "LDS budget");
-static_assert(Wgrad8Tile::L + kWgradStores < 64, "vmcnt range");
+static_assert(Wgrad8Tile::L + wgrad_stores<true>() < 64, "vmcnt range");
 
-// Epilogue with 32 x 64 staging passes and bounds-checked buffer stores: lanes outside the
-// weight matrix get an offset past the buffer's end, which the hardware drops, so every
-// wavefront issues exactly kWgradStores stores per tile (the kernel's vmcnt waits count them).
-template <int TM, int TN, int WTM, int WTN>
+// Epilogue with 32 x 64 (bf16) or 32 x 32 (fp32) staging passes and bounds-checked buffer stores:
+// lanes outside the weight matrix get an offset past the buffer's end, which the hardware drops,
+// so every wavefront issues exactly wgrad_stores<F32>() stores per tile (the kernel's vmcnt waits
+// count them).
+template <bool F32, int TM, int TN, int WTM, int WTN>
 __device__ __forceinline__ void store_wgrad8(const GemmArgs& p, const f32x16_t (&acc)[TM][TN],
                                              int g, int m0, int n0, int wm, int wn, int lane,
                                              unsigned char* scr) {
-  static_assert(TM * (TN / 2) * 4 == kWgradStores, "store count");
-  uint16_t* out = p.out + (int64_t)g * p.o_gstride;
-  const uint32_t bytes = (uint32_t)((int64_t)p.M * p.ldo * 2);
+  static_assert(TM * (F32 ? TN : TN / 2) * 4 == wgrad_stores<F32>(), "store count");
+  constexpr int EB = F32 ? 4 : 2;   // bytes per element
+  unsigned char* out = reinterpret_cast<unsigned char*>(p.out) + (int64_t)g * p.o_gstride * EB;
+  const uint32_t bytes = (uint32_t)((int64_t)p.M * p.ldo * EB);
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(out, 0, (int)bytes, 0x00020000);
+  typedef uint32_t v4_t __attribute__((ext_vector_type(4)));
+  auto put = [&](int m, int col, v4_t v) {
+    const uint32_t off =
+        (m < p.M && col < p.N) ? (uint32_t)(((int64_t)m * p.ldo + col) * EB) : 0x80000000u;
+    // non-temporal: dW is written once and read by no later kernel here, so it should not evict
+    // the activation panels the next tiles read from L2
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStoreNT);
+  };
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    const int mrow = m0 + wm * WTM + i * 32;
+    if constexpr (F32) {
 #pragma unroll
-    for (int h = 0; h < TN / 2; ++h) {
-      const int mrow = m0 + wm * WTM + i * 32, c0 = n0 + wn * WTN + h * 64;
-      stage_bf16<2>(scr, lane, [&](int j, int q, int e) { return acc[i][2 * h + j][4 * q + e]; },
-          [&](int rr, int c, uint4 d) {
-            const int m = mrow + rr, col = c0 + c;
-            const uint32_t off =
-                (m < p.M && col < p.N) ? (uint32_t)(((int64_t)m * p.ldo + col) * 2) : 0x80000000u;
-            typedef uint32_t v4_t __attribute__((ext_vector_type(4)));
-            const v4_t v = {d.x, d.y, d.z, d.w};
-            // non-temporal: dW is written once and read by no later kernel here, so it should
-            // not evict the activation panels the next tiles read from L2
-            __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStoreNT);
-          });
+      for (int j = 0; j < TN; ++j) {
+        const int c0 = n0 + wn * WTN + j * 32;
+        stage_f32<1>(scr, lane, [&](int, int q, int e) { return acc[i][j][4 * q + e]; },
+            [&](int rr, int c, float4 d) {
+              const v4_t v = {__float_as_uint(d.x), __float_as_uint(d.y), __float_as_uint(d.z),
+                              __float_as_uint(d.w)};
+              put(mrow + rr, c0 + c, v);
+            });
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < TN / 2; ++h) {
+        const int c0 = n0 + wn * WTN + h * 64;
+        stage_bf16<2>(scr, lane, [&](int j, int q, int e) { return acc[i][2 * h + j][4 * q + e]; },
+            [&](int rr, int c, uint4 d) {
+              const v4_t v = {d.x, d.y, d.z, d.w};
+              put(mrow + rr, c0 + c, v);
+            });
+      }
     }
+  }
 }
 
 // A wave-uniform read of a read-only int array through the scalar data cache (the constant
@@ -1253,12 +1276,12 @@ __device__ __forceinline__ int ld_scalar(const int32_t* a, int64_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)a)[i];
 }
 
-template <int KIND>
+template <int KIND, bool F32>
 __global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
   typedef Wgrad8Tile TL;
   typedef Eng8<KIND, TL> E;
-  constexpr int S = kWgradStores, L = TL::L;
+  constexpr int S = wgrad_stores<F32>(), L = TL::L;
   const int64_t per_g = (int64_t)p.n_tiles_m * p.n_tiles_n, total = per_g * p.G;
   const int64_t per_x = (total + kNumXcd - 1) / kNumXcd;   // each XCD walks a contiguous range
   const int xcd = blockIdx.x % kNumXcd, nwg = gridDim.x / kNumXcd;
@@ -1330,7 +1353,7 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) 
     };
     if (cur.nk > 0) e.template run<S, true>(acc, dc, cur.nk, s0, stores, dn, chain, at_end);
     else at_end();
-    store_wgrad8<TL::TM, TL::TN, TL::WTM, TL::WTN>(p, acc, cur.g, cur.m0, cur.n0, e.wm, e.wn,
+    store_wgrad8<F32, TL::TM, TL::TN, TL::WTM, TL::WTN>(p, acc, cur.g, cur.m0, cur.n0, e.wm, e.wn,
                                                    e.lane, scr);
     if (!has_next) break;
     s0 = chain ? (s0 + cur.nk) & 1 : 0;
@@ -1451,41 +1474,49 @@ hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap
   return launch_rows<kDgradGateUp>(g, mcap, st);
 }
 
+namespace {
+template <int KIND>
+hipError_t launch_wgrad_kind(const GemmArgs& g, bool f32, hipStream_t st) {
+  const int64_t tiles = (int64_t)g.G * g.n_tiles_m * g.n_tiles_n;
+  if (f32)
+    hipLaunchKernelGGL((ggemm_wgrad8_kernel<KIND, true>), dim3(persistent_grid(tiles)),
+                       dim3(kThreads8), 0, st, g);
+  else
+    hipLaunchKernelGGL((ggemm_wgrad8_kernel<KIND, false>), dim3(persistent_grid(tiles)),
+                       dim3(kThreads8), 0, st, g);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_ggemm_wgrad(const moe_shape_t& s, uint32_t which, const uint16_t* x_perm,
                               const uint16_t* a,
                               const uint16_t* dy_perm, const uint16_t* dh,
-                              const int32_t* seg_offsets, uint16_t* dw1, uint16_t* dw2,
+                              const int32_t* seg_offsets, void* dw1, void* dw2, bool f32,
                               hipStream_t st) {
   GemmArgs g{};
   g.I = s.I;
   g.G = s.E + s.S;
   g.seg = seg_offsets;
-  // dW2[g] [H, I] = dy_perm_seg^T . a_seg
-  g.a = dy_perm; g.lda = s.H;
-  g.b = a; g.ldb = s.I;
-  g.out = dw2; g.ldo = s.I; g.o_gstride = (int64_t)s.H * s.I;
-  g.M = s.H; g.N = s.I;
-  g.n_tiles_m = (g.M + Wgrad8Tile::BM - 1) / Wgrad8Tile::BM;
-  g.n_tiles_n = (g.N + Wgrad8Tile::BN - 1) / Wgrad8Tile::BN;
-  int64_t tiles = (int64_t)g.G * g.n_tiles_m * g.n_tiles_n;
   if (which & MOE_WGRAD_DOWN) {
-    hipLaunchKernelGGL((ggemm_wgrad8_kernel<kWgradDown>), dim3(persistent_grid(tiles)),
-                       dim3(kThreads8), 0, st, g);
-    hipError_t e = hipGetLastError();
+    // dW2[g] [H, I] = dy_perm_seg^T . a_seg
+    g.a = dy_perm; g.lda = s.H;
+    g.b = a; g.ldb = s.I;
+    g.out = static_cast<uint16_t*>(dw2); g.ldo = s.I; g.o_gstride = (int64_t)s.H * s.I;
+    g.M = s.H; g.N = s.I;
+    g.n_tiles_m = (g.M + Wgrad8Tile::BM - 1) / Wgrad8Tile::BM;
+    g.n_tiles_n = (g.N + Wgrad8Tile::BN - 1) / Wgrad8Tile::BN;
+    const hipError_t e = launch_wgrad_kind<kWgradDown>(g, f32, st);
     if (e != hipSuccess) return e;
   }
   if (!(which & MOE_WGRAD_GATEUP)) return hipSuccess;
   // dW1[g] [2I, H] = dh_seg^T . x_perm_seg
   g.a = dh; g.lda = 2 * (int64_t)s.I;
   g.b = x_perm; g.ldb = s.H;
-  g.out = dw1; g.ldo = s.H; g.o_gstride = (int64_t)2 * s.I * s.H;
+  g.out = static_cast<uint16_t*>(dw1); g.ldo = s.H; g.o_gstride = (int64_t)2 * s.I * s.H;
   g.M = 2 * s.I; g.N = s.H;
   g.n_tiles_m = (g.M + Wgrad8Tile::BM - 1) / Wgrad8Tile::BM;
   g.n_tiles_n = (g.N + Wgrad8Tile::BN - 1) / Wgrad8Tile::BN;
-  tiles = (int64_t)g.G * g.n_tiles_m * g.n_tiles_n;
-  hipLaunchKernelGGL((ggemm_wgrad8_kernel<kWgradGateUp>), dim3(persistent_grid(tiles)),
-                     dim3(kThreads8), 0, st, g);
-  return hipGetLastError();
+  return launch_wgrad_kind<kWgradGateUp>(g, f32, st);
 }
 
 }  // namespace moe

@@ -36,9 +36,10 @@ hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap
                               const int32_t* total_rows, const uint16_t* w1, const uint16_t* w2,
                               uint16_t* dh, uint16_t* dx_perm, hipStream_t st);
 
+// dW1/dW2 are bf16 (f32 == false) or fp32 (f32 == true) arrays of the same shapes.
 hipError_t launch_ggemm_wgrad(const moe_shape_t& s, uint32_t which, const uint16_t* x_perm, const uint16_t* a,
                               const uint16_t* dy_perm, const uint16_t* dh,
-                              const int32_t* seg_offsets, uint16_t* dw1, uint16_t* dw2,
+                              const int32_t* seg_offsets, void* dw1, void* dw2, bool f32,
                               hipStream_t st);
 
 hipError_t launch_combine(const moe_shape_t& s, const uint16_t* y_perm, const int32_t* pos,

@@ -166,6 +166,18 @@ moe_status_t grouped_gemm_bwd(const moe_shape_t* shape, uint32_t which, const ui
                               void* stream);
 
 /*
+ * grouped_gemm_wgrad_f32 — the weight gradients of grouped_gemm_bwd (MOE_WGRAD_DOWN and/or
+ * MOE_WGRAD_GATEUP in `which`, no other bits) with fp32 dW outputs instead of bf16: the same fp32
+ * accumulation over each group's segment, stored without rounding to bf16 (for optimizers that
+ * keep fp32 gradients). dw1 [G,2I,H] and dw2 [G,H,I] are fp32, 16-byte aligned; the inputs and
+ * their layouts are grouped_gemm_bwd's. Empty segments give zero gradients. Errors as there.
+ */
+moe_status_t grouped_gemm_wgrad_f32(const moe_shape_t* shape, uint32_t which, const uint16_t* x_perm,
+                                    const uint16_t* a, const uint16_t* dy_perm, const uint16_t* dh,
+                                    const int32_t* seg_offsets, float* dw1, float* dw2,
+                                    void* stream);
+
+/*
  * moe_combine — weighted unpermute: y[t] = bf16( sum_j topk_w[t,j] * y_perm[pos[t,j]]
  *               + sum_s y_perm[seg_offsets[E+s] + t] ), fp32 sum in slot order, shared last
  * (shared experts weigh 1: TR section A2, always active).

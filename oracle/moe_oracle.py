@@ -81,11 +81,18 @@ def _identity(v):
     return np.asarray(v, dtype=np.float64)
 
 
+def round_fp32(v) -> np.ndarray:
+    """Round float64 values to the nearest fp32 value (returned as float64)."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
 def _rounder(rnd):
     if rnd is None:
         return _identity
     if rnd == "bf16":
         return round_bf16
+    if rnd == "fp32":
+        return round_fp32
     return rnd
 
 
@@ -363,7 +370,8 @@ def expert_ffn_dgrad(dy_perm, h, seg_offsets, w1, w2, I: int, rnd="bf16"):
 
 def expert_ffn_wgrad(x_perm, a, dy_perm, dh, seg_offsets, I: int, H: int, rnd="bf16"):
     """wgrad per group: dW2_g = dy_perm_seg^T a_seg [H,I]; dW1_g = dh_seg^T x_perm_seg [2I,H].
-    A group with an empty segment gets zeros."""
+    A group with an empty segment gets zeros. rnd="fp32" gives the fp32-gradient variant (the
+    same sums stored in fp32 instead of bf16)."""
     R = _rounder(rnd)
     seg = np.asarray(seg_offsets, dtype=np.int64)
     G = len(seg) - 1

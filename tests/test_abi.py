@@ -128,6 +128,22 @@ def test_router_backward_and_bias_update_checks(lib):
         assert "gamma" in M.moe_last_error()
 
 
+def test_fp32_wgrad_checks(lib):
+    s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
+    d, odd = ctypes.c_void_p(16), ctypes.c_void_p(24)
+    assert lib.grouped_gemm_wgrad_f32(ctypes.byref(s), M.MOE_DGRAD_DOWN, *([d] * 7), None) == -1
+    assert lib.grouped_gemm_wgrad_f32(ctypes.byref(s), 0, *([d] * 7), None) == -1
+    for i in range(7):   # x_perm, a, dy_perm, dh, seg_offsets, dw1, dw2 all needed for both kinds
+        a = [d] * 7
+        a[i] = None
+        assert lib.grouped_gemm_wgrad_f32(ctypes.byref(s), M.MOE_WGRAD, *a, None) == -1, i
+    for i in (0, 1, 2, 3, 5, 6):
+        a = [d] * 7
+        a[i] = odd
+        assert lib.grouped_gemm_wgrad_f32(ctypes.byref(s), M.MOE_WGRAD, *a, None) == -1, i
+        assert "aligned" in M.moe_last_error()
+
+
 def test_gemm_tensors_must_be_16_byte_aligned(lib):
     s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
     d, odd = ctypes.c_void_p(16), ctypes.c_void_p(16 + 8)
