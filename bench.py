@@ -336,6 +336,18 @@ def main():
     if router_bwd is not None:
         out["router_backward"] = router_bwd
     if args.workload == "c2":
+        # The fp32-gradient variant of the two weight-gradient GEMMs on the step's own operands.
+        dw1f = torch.empty(E, 2 * I, H, device=dev)
+        dw2f = torch.empty(E, H, I, device=dev)
+        wg32 = {}
+        for name, which in (("wgrad_down", M.MOE_WGRAD_DOWN), ("wgrad_gateup", M.MOE_WGRAD_GATEUP)):
+            t = _time_call(torch, np, lambda: M.grouped_gemm_wgrad_f32(
+                s, which, b["x_perm"], b["a"], b["dy_perm"], b["dh"], b["seg_offsets"], dw1f, dw2f),
+                10)
+            wg32[name] = {"ms": round(t, 4),
+                          "tflops": round(per_row[name] * rows / (t * 1e-3) / 1e12, 1)}
+        out["wgrad_fp32_dw"] = wg32
+        del dw1f, dw2f
         # Context only: the gate/up product as a plain batched library GEMM (torch.bmm, served by
         # hipBLASLt) over the 128 experts' 384-row segments, operands made contiguous first.
         Xb = b["x_perm"][:T * K].view(E, T * K // E, H)
