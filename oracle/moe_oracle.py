@@ -445,6 +445,38 @@ def router_input_grad(dlogits, w_gate) -> np.ndarray:
     return (dz @ np.asarray(w_gate, dtype=np.float32).astype(np.float64)).astype(np.float32)
 
 
+def balance_loss(probs, topk_idx, seq_len: int, alpha: float):
+    """Sequence-wise balance loss and its gradient with respect to the router logits.
+
+    The pages add a sequence-wise balance loss to keep any one sequence from routing too unevenly
+    but give no formula. Reading (the form of the cited aux-loss-free method family): the batch is
+    T / seq_len sequences of seq_len consecutive tokens; in each sequence
+        f_e = E / (K * seq_len) * #{(t, j) in the sequence : topk_idx[t, j] = e}   (1 when balanced)
+        P_e = mean over the sequence's tokens of p[t, e]
+        L_seq = alpha * sum_e f_e P_e,
+    and the batch loss is the mean of L_seq over the sequences. The selection counts f are piecewise
+    constant in the logits, so the gradient flows through P only:
+        dL/dp[t, e] = alpha f_e / (seq_len * n_seq), then through the softmax as in route_backward.
+    Returns (per-sequence losses [n_seq] float64, dlogits [T,E] float64).
+    """
+    p = np.asarray(probs, dtype=np.float32).astype(np.float64)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, E = p.shape
+    K = idx.shape[1]
+    n_seq = T // seq_len
+    losses = np.zeros(n_seq)
+    dz = np.zeros((T, E))
+    for q in range(n_seq):
+        t0, t1 = q * seq_len, (q + 1) * seq_len
+        f = np.bincount(idx[t0:t1].reshape(-1), minlength=E) * (E / (K * seq_len))
+        P = p[t0:t1].mean(axis=0)
+        losses[q] = alpha * float(f @ P)
+        g = np.broadcast_to(alpha * f / (seq_len * n_seq), (seq_len, E))
+        pq = p[t0:t1]
+        dz[t0:t1] = pq * (g - (pq * g).sum(axis=1, keepdims=True))
+    return losses, dz
+
+
 def bias_update(sel_bias, counts, T: int, K: int, gamma: float) -> np.ndarray:
     """One step of the aux-loss-free balance: b_e + gamma * sign(mean load - c_e), in fp32.
 

@@ -15,7 +15,8 @@ from oracle import moe_oracle as O
 _ORIG = {name: getattr(O, name) for name in (
     "softmax_probs", "selection_keys", "select_topk", "expert_counts", "permute_maps",
     "expert_ffn_rows", "combine", "combine_backward", "swiglu_backward", "expert_ffn_dgrad",
-    "expert_ffn_wgrad", "round_bf16", "route_backward", "router_weight_grad", "bias_update")}
+    "expert_ffn_wgrad", "round_bf16", "route_backward", "router_weight_grad", "bias_update",
+    "balance_loss")}
 
 
 # --- routing --------------------------------------------------------------------------------------
@@ -175,6 +176,21 @@ def router_weight_grad_mean(dlogits, x_bits):
     return (dw / np.float32(np.asarray(dlogits).shape[0])).astype(np.float32)
 
 
+def balance_loss_summed(probs, topk_idx, seq_len, alpha):
+    # gradient of the sum over sequences while the loss reported is their mean
+    losses, dz = _ORIG["balance_loss"](probs, topk_idx, seq_len, alpha)
+    return losses, dz * (np.asarray(probs).shape[0] // seq_len)
+
+
+def balance_loss_raw_counts(probs, topk_idx, seq_len, alpha):
+    # f as raw counts, without the E / (K seq_len) normalisation
+    p = np.asarray(probs, np.float32)
+    K = np.asarray(topk_idx).shape[1]
+    scale = p.shape[1] / (K * seq_len)
+    losses, dz = _ORIG["balance_loss"](probs, topk_idx, seq_len, alpha / scale)
+    return losses, dz
+
+
 def bias_update_sign_flipped(sel_bias, counts, T, K, gamma):
     return _ORIG["bias_update"](sel_bias, counts, T, K, -gamma)
 
@@ -242,6 +258,11 @@ MUTANTS = {
     "bias_update_sign_flipped": ("bias_update", bias_update_sign_flipped,
                                  ["test_oracle_route_bwd.py::test_bias_update_hand_worked",
                                   "test_oracle_route_bwd.py::test_bias_update_is_one_fp32_add"]),
+    "balance_loss_summed": ("balance_loss", balance_loss_summed,
+                            ["test_oracle_route_bwd.py::test_balance_loss_gradient_matches_autograd",
+                             "test_oracle_route_bwd.py::test_balance_loss_finite_differences"]),
+    "balance_loss_raw_counts": ("balance_loss", balance_loss_raw_counts,
+                                ["test_oracle_route_bwd.py::test_balance_loss_closed_forms"]),
     "round_toward_zero": ("round_bf16", round_toward_zero,
                           ["test_oracle_numerics.py::test_round_bf16_known_values",
                            "test_oracle_numerics.py::test_round_bf16_matches_torch_on_fp32_inputs"]),

@@ -122,3 +122,76 @@ def test_bias_update_is_one_fp32_add():
     assert np.all(np.abs(step[moved] - np.float64(np.float32(1e-3))) <= 0.5 * np.maximum(ulp, np.spacing(np.abs(got)))[moved] + 1e-12)
     assert np.all(got[~moved] == b[~moved])
     assert np.all((got > b) == (counts < 384))
+
+
+# --- sequence-wise balance loss ------------------------------------------------------------------
+def _balance_autograd(p, idx, seq_len, alpha):
+    """float64 autograd of the loss definition at the logits log(p) (the counts f held fixed)."""
+    T, E = p.shape
+    K = idx.shape[1]
+    zt = torch.tensor(np.log(p.astype(np.float64)), dtype=torch.float64, requires_grad=True)
+    pt = torch.softmax(zt, dim=1)
+    n_seq = T // seq_len
+    total = 0
+    for q in range(n_seq):
+        sl = slice(q * seq_len, (q + 1) * seq_len)
+        f = torch.tensor(np.bincount(idx[sl].reshape(-1), minlength=E) * (E / (K * seq_len)),
+                         dtype=torch.float64)
+        total = total + alpha * (f * pt[sl].mean(dim=0)).sum()
+    (total / n_seq).backward()
+    return zt.grad.numpy()
+
+
+@pytest.mark.parametrize("T,E,K,seq_len", [(64, 8, 2, 16), (96, 128, 6, 96), (40, 20, 4, 8)])
+def test_balance_loss_gradient_matches_autograd(T, E, K, seq_len):
+    z, p, idx, _ = _routing(T, E, K, seed=T + E)
+    _, dz = O.balance_loss(p, idx, seq_len, 1e-2)
+    ref = _balance_autograd(p, idx, seq_len, 1e-2)
+    # the probabilities are fp32, so their softmax-of-log reproduction sums to 1 only to fp32 accuracy
+    np.testing.assert_allclose(dz, ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max())
+
+
+def test_balance_loss_finite_differences():
+    T, E, K, seq_len, alpha = 12, 6, 2, 4, 0.3
+    z, p, idx, _ = _routing(T, E, K, seed=21)
+    z64 = np.log(p.astype(np.float64))
+    f = [np.bincount(idx[q * seq_len:(q + 1) * seq_len].reshape(-1), minlength=E) * (E / (K * seq_len))
+         for q in range(T // seq_len)]
+
+    def loss(zz):
+        ez = np.exp(zz - zz.max(axis=1, keepdims=True))
+        pp = ez / ez.sum(axis=1, keepdims=True)
+        return np.mean([alpha * f[q] @ pp[q * seq_len:(q + 1) * seq_len].mean(axis=0)
+                        for q in range(T // seq_len)])
+
+    h = 1e-6
+    fd = np.zeros((T, E))
+    for t in range(T):
+        for e in range(E):
+            zp, zm = z64.copy(), z64.copy()
+            zp[t, e] += h
+            zm[t, e] -= h
+            fd[t, e] = (loss(zp) - loss(zm)) / (2 * h)
+    _, dz = O.balance_loss(p, idx, seq_len, alpha)
+    np.testing.assert_allclose(dz, fd, rtol=1e-5, atol=1e-10)
+
+
+def test_balance_loss_closed_forms():
+    T, E, K, seq_len, alpha = 64, 8, 2, 32, 0.5
+    # perfectly balanced routing with uniform affinities: f = 1, P = 1/E, so L = alpha
+    idx = ((K * np.arange(T)[:, None] + np.arange(K)[None, :]) % E).astype(np.int32)
+    p = np.full((T, E), 1.0 / E, np.float32)
+    losses, dz = O.balance_loss(p, idx, seq_len, alpha)
+    np.testing.assert_allclose(losses, alpha, rtol=1e-7)
+    assert np.abs(dz).max() <= 1e-12          # uniform p: the softmax passes no gradient
+    # collapse: every token on experts 0..K-1 with p = 1/K there: f = E/K, P = 1/K, L = alpha E / K
+    idx = np.tile(np.arange(K, dtype=np.int32), (T, 1))
+    p = np.zeros((T, E), np.float32)
+    p[:, :K] = 1.0 / K
+    losses, _ = O.balance_loss(p, idx, seq_len, alpha)
+    np.testing.assert_allclose(losses, alpha * E / K, rtol=1e-7)
+    # the gradient sums to zero over the experts (softmax; the fp32 probabilities sum to 1 only to
+    # fp32 accuracy)
+    z, p, idx, _ = _routing(T, E, K, seed=2)
+    _, dz = O.balance_loss(p, idx, seq_len, alpha)
+    assert np.abs(dz.sum(axis=1)).max() <= 1e-6 * np.abs(dz).max()
