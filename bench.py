@@ -146,7 +146,8 @@ def _time_call(torch, np, fn, reps):
 
 def router_backward_timing(torch, np, M, Sy, cfg, s, b, X, dev, reps=20):
     """The router backward on the step's own routing and weight gradients (not part of the step):
-    dlogits alone, then with dWg = dlogits^T x and dx_router = dlogits Wg; and the bias update."""
+    dlogits alone, then with dWg = dlogits^T x and dx_router = dlogits Wg; the bias update; the
+    sequence-wise balance loss with its gradient."""
     T, H, E = cfg.T, cfg.H, cfg.E
     WG = torch.from_numpy(Sy.draw_wg(cfg)).to(dev)
     dz = torch.empty(T, E, device=dev)
@@ -159,11 +160,16 @@ def router_backward_timing(torch, np, M, Sy, cfg, s, b, X, dev, reps=20):
     t_dx = _time_call(torch, np, lambda: M.moe_route_bwd(*args, None, dxr), reps) - t_dz
     t_all = _time_call(torch, np, lambda: M.moe_route_bwd(*args, dwg, dxr), reps)
     t_bias = _time_call(torch, np, lambda: M.moe_bias_update(s, b["expert_counts"], 1e-3, sb), reps)
+    loss = torch.empty(1, device=dev)   # the batch as one sequence of T tokens (8K, the pages' length)
+    ws = torch.empty(M.moe_balance_workspace_size(s, T) // 4, device=dev)
+    t_bal = _time_call(torch, np, lambda: M.moe_balance_loss(s, T, 1e-3, b["probs"], b["topk_idx"],
+                                                             loss, dz, ws), reps)
     flops = 2.0 * T * E * H                # each of dWg and dx_router, fp32
     return {"ms": round(t_all, 4), "dlogits_ms": round(t_dz, 4),
             "dwg_ms": round(t_dwg, 4), "dwg_tflops": round(flops / (t_dwg * 1e-3) / 1e12, 2),
             "dx_ms": round(t_dx, 4), "dx_tflops": round(flops / (t_dx * 1e-3) / 1e12, 2),
-            "fp32_peak_tflops": PEAK_FP32_TFLOPS, "bias_update_ms": round(t_bias, 4)}
+            "fp32_peak_tflops": PEAK_FP32_TFLOPS, "bias_update_ms": round(t_bias, 4),
+            "balance_loss_ms": round(t_bal, 4)}
 
 
 def main():

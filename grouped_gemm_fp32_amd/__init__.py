@@ -18,7 +18,8 @@ __all__ = [
     "moe_abi_version", "moe_status_string", "moe_last_error", "moe_row_capacity",
     "moe_workspace_size", "moe_route", "moe_permute", "grouped_gemm_fwd", "grouped_gemm_bwd",
     "grouped_gemm_wgrad_f32", "moe_combine", "moe_combine_bwd", "moe_unpermute_bwd",
-    "moe_route_bwd", "moe_bias_update",
+    "moe_route_bwd", "moe_router_grads", "moe_balance_loss",
+    "moe_balance_workspace_size", "moe_bias_update",
     "make_shape", "alloc_buffers",
 ]
 
@@ -80,6 +81,10 @@ _SIGS = {
     "moe_unpermute_bwd": (ctypes.c_int, [_SP] + [_P] * 5),
     "moe_route_bwd": (ctypes.c_int, [_SP] + [_P] * 9),
     "grouped_gemm_wgrad_f32": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 8),
+    "moe_router_grads": (ctypes.c_int, [_SP] + [_P] * 6),
+    "moe_balance_loss": (ctypes.c_int, [_SP, ctypes.c_int32, ctypes.c_float] + [_P] * 5
+                         + [ctypes.c_size_t, _P]),
+    "moe_balance_workspace_size": (ctypes.c_size_t, [_SP, ctypes.c_int32]),
     "moe_bias_update": (ctypes.c_int, [_SP, _P, ctypes.c_float, _P, _P]),
 }
 
@@ -274,6 +279,29 @@ def moe_route_bwd(shape, dtopk_w, topk_idx, probs, x, w_gate, dlogits, dw_gate, 
         _ptr(probs, "probs", _f32()), _ptr(x, "x", _bf16()), _ptr(w_gate, "w_gate", _f32()),
         _ptr(dlogits, "dlogits", _f32()), _ptr(dw_gate, "dw_gate", _f32()),
         _ptr(dx_router, "dx_router", _f32()), st))
+
+
+def moe_router_grads(shape, dlogits, x, w_gate, dw_gate, dx_router, stream=None):
+    lib = load_library()
+    st = _stream(stream, dlogits, dw_gate, dx_router)
+    _check("moe_router_grads", lib.moe_router_grads(
+        ctypes.byref(shape), _ptr(dlogits, "dlogits", _f32()), _ptr(x, "x", _bf16()),
+        _ptr(w_gate, "w_gate", _f32()), _ptr(dw_gate, "dw_gate", _f32()),
+        _ptr(dx_router, "dx_router", _f32()), st))
+
+
+def moe_balance_workspace_size(shape, seq_len) -> int:
+    return int(load_library().moe_balance_workspace_size(ctypes.byref(shape), int(seq_len)))
+
+
+def moe_balance_loss(shape, seq_len, alpha, probs, topk_idx, seq_loss, dlogits, ws, stream=None):
+    lib = load_library()
+    st = _stream(stream, probs, seq_loss, dlogits)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("moe_balance_loss", lib.moe_balance_loss(
+        ctypes.byref(shape), int(seq_len), float(alpha), _ptr(probs, "probs", _f32()),
+        _ptr(topk_idx, "topk_idx", _i32()), _ptr(seq_loss, "seq_loss", _f32()),
+        _ptr(dlogits, "dlogits", _f32()), _ptr(ws, "ws"), ws_bytes, st))
 
 
 def moe_bias_update(shape, expert_counts, gamma, sel_bias, stream=None):

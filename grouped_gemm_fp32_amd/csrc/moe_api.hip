@@ -350,6 +350,53 @@ moe_status_t moe_route_bwd(const moe_shape_t* s, const float* dtopk_w, const int
                     "moe_route_bwd");
 }
 
+moe_status_t moe_router_grads(const moe_shape_t* s, const float* dlogits, const uint16_t* x,
+                              const float* w_gate, float* dw_gate, float* dx_router, void* stream) {
+  CHECK_SHAPE(s);
+  if (s->T > 0) {
+    REQUIRE(dlogits);
+    if (dw_gate) REQUIRE_T(x);
+    if (dx_router) REQUIRE(w_gate);
+  }
+  return hip_status(moe::launch_router_grads(*s, dlogits, x, w_gate, dw_gate, dx_router,
+                                             (hipStream_t)stream),
+                    "moe_router_grads");
+}
+
+size_t moe_balance_workspace_size(const moe_shape_t* s, int32_t seq_len) {
+  if (check_shape(s) != MOE_OK || seq_len < 1 || s->T % seq_len != 0) return 0;
+  return sizeof(float) * (size_t)moe::balance_workspace_floats(s->T, seq_len, s->E);
+}
+
+moe_status_t moe_balance_loss(const moe_shape_t* s, int32_t seq_len, float alpha, const float* probs,
+                              const int32_t* topk_idx, float* seq_loss, float* dlogits, void* ws,
+                              size_t ws_bytes, void* stream) {
+  CHECK_SHAPE(s);
+  if (seq_len < 1 || s->T % seq_len != 0) {
+    set_err("seq_len must be >= 1 and divide T");
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (!(alpha >= 0.0f) || alpha > 3.0e38f) {
+    set_err("alpha must be a finite number >= 0");
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (!seq_loss && !dlogits) {
+    set_err("nothing to compute: seq_loss and dlogits are both NULL");
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (s->T == 0) return MOE_OK;
+  REQUIRE(probs);
+  REQUIRE(topk_idx);
+  REQUIRE(ws);
+  if (ws_bytes < sizeof(float) * (size_t)moe::balance_workspace_floats(s->T, seq_len, s->E)) {
+    set_err("workspace smaller than moe_balance_workspace_size()");
+    return MOE_ERR_WORKSPACE;
+  }
+  return hip_status(moe::launch_balance_loss(*s, seq_len, alpha, probs, topk_idx, seq_loss, dlogits,
+                                             static_cast<float*>(ws), (hipStream_t)stream),
+                    "moe_balance_loss");
+}
+
 moe_status_t moe_bias_update(const moe_shape_t* s, const int32_t* expert_counts, float gamma,
                              float* sel_bias, void* stream) {
   CHECK_SHAPE(s);

@@ -59,6 +59,17 @@ hipError_t launch_route_bwd(const moe_shape_t& s, const float* dtopk_w, const in
                             const float* probs, const uint16_t* x, const float* wg, float* dlogits,
                             float* dw_gate, float* dx_router, hipStream_t st);
 
+hipError_t launch_router_grads(const moe_shape_t& s, const float* dlogits, const uint16_t* x,
+                               const float* wg, float* dw_gate, float* dx_router, hipStream_t st);
+
+// 4-byte words of scratch moe_balance_loss needs (per 256-token chunk of each sequence: a partial
+// loss and E selection counts)
+int64_t balance_workspace_floats(int T, int seq_len, int E);
+
+hipError_t launch_balance_loss(const moe_shape_t& s, int seq_len, float alpha, const float* probs,
+                               const int32_t* topk_idx, float* seq_loss, float* dlogits, float* ws,
+                               hipStream_t st);
+
 hipError_t launch_bias_update(const moe_shape_t& s, const int32_t* counts, float gamma, float* bias,
                               hipStream_t st);
 

@@ -18,6 +18,11 @@
 //                       sums are added in wavefront order (deterministic).
 //   router_dx_kernel    dx_router[T,H] = dlogits Wg, the same instruction with the contraction
 //                       over the experts: a 64-token tile of dlogits in LDS, Wg read from L2.
+//   balance_hist_kernel, balance_kernel, balance_reduce_kernel
+//                       per-chunk selection counts, then the sequence-wise balance loss (per sequence alpha sum_e f_e P_e, f the
+//                       normalised selection counts, P the mean probabilities) as per-chunk
+//                       partial sums reduced in a fixed order, and its gradient, added to dlogits:
+//                       p_e (g_e - sum_i p_i g_i) with g = alpha f / (seq_len n_seq).
 //   bias_update_kernel  b_e += gamma * sign(T K - E c_e), one fp32 add per expert.
 #include "moe_common.h"
 #include "moe_internal.h"
@@ -207,6 +212,102 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(int T, int H, int E
   }
 }
 
+// ---- sequence-wise balance loss ---------------------------------------------------------------------
+// Per sequence of seq_len consecutive tokens: f_e = E / (K seq_len) * (selections of e), P_e = mean
+// of p[t, e], loss = alpha sum_e f_e P_e; the batch loss is the mean over the n_seq sequences.
+constexpr int kBalTok = 256;       // tokens per workgroup
+constexpr int kBalThreads = 1024;  // balance_kernel: 16 wavefronts, 16 tokens each
+
+// Selection counts of chunk c of sequence q (its kBalTok tokens): hc[(q * n_chunk + c) * E + e].
+// Entries outside 0..E-1 are not counted.
+__global__ __launch_bounds__(kThreads) void balance_hist_kernel(int seq_len, int E, int K,
+                                                                const int32_t* __restrict__ topk_idx,
+                                                                int32_t* __restrict__ hc) {
+  __shared__ int hist[256];
+  for (int e = threadIdx.x; e < E; e += kThreads) hist[e] = 0;
+  __syncthreads();
+  const int q = blockIdx.y, c = blockIdx.x;
+  const int t0 = c * kBalTok, t1 = min(seq_len, t0 + kBalTok);
+  const int64_t base = ((int64_t)q * seq_len + t0) * K;
+  for (int i = threadIdx.x; i < (t1 - t0) * K; i += kThreads) {
+    const int e = topk_idx[base + i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);   // integer adds: order-free
+  }
+  __syncthreads();
+  int32_t* out = hc + ((int64_t)q * gridDim.x + c) * E;
+  for (int e = threadIdx.x; e < E; e += kThreads) out[e] = hist[e];
+}
+
+// Workgroup (chunk, q) covers kBalTok tokens of sequence q, one wavefront per token. With f the
+// sequence's normalised counts, L_seq = alpha sum_e f_e P_e = (alpha / seq_len) sum_t <f, p_t>:
+// each token's <f, p_t> goes into the workgroup's partial sum (wavefront order, then token order
+// within a wavefront), written to part[q * n_chunk + chunk]. With dlogits, the gradient of the
+// mean loss is added: g = alpha f / (seq_len n_seq), dlogits[t, e] += p_e (g_e - <p_t, g>).
+__global__ __launch_bounds__(kBalThreads) void balance_kernel(int seq_len, int n_seq, int E, int K,
+                                                           float alpha,
+                                                           const float* __restrict__ probs,
+                                                           const int32_t* __restrict__ hc,
+                                                           float* __restrict__ dlogits,
+                                                           float* __restrict__ part) {
+  __shared__ int hist[256];
+  __shared__ float wpart[kBalThreads / 64];
+  const int q = blockIdx.y;
+  for (int e = threadIdx.x; e < E; e += kBalThreads) hist[e] = 0;
+  __syncthreads();
+  // the sequence's counts from its chunks' (integer adds: order-free)
+  const int64_t hbase = (int64_t)q * gridDim.x * E;
+  for (int i = threadIdx.x; i < (int)gridDim.x * E; i += kBalThreads)
+    atomicAdd(&hist[i % E], hc[hbase + i]);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float fs = (float)E / (float)(K * seq_len);               // f_e = fs * count_e
+  const float gs = alpha / ((float)seq_len * (float)n_seq);        // g_e = gs * f_e
+  float f[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int e = lane + 64 * s;
+    f[s] = e < E ? fs * (float)hist[e] : 0.0f;
+  }
+  float acc = 0.0f;
+  const int t_end = min(seq_len, (blockIdx.x + 1) * kBalTok);
+  for (int tl = blockIdx.x * kBalTok + wave; tl < t_end; tl += kBalThreads / 64) {
+    const int64_t t = (int64_t)q * seq_len + tl;
+    float p[4], dot = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int e = lane + 64 * s;
+      p[s] = e < E ? probs[t * E + e] : 0.0f;
+      dot += p[s] * f[s];
+    }
+    dot = wave_sum(dot);   // <f, p_t>, the same on every lane
+    acc += dot;
+    if (dlogits) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int e = lane + 64 * s;
+        if (e < E) dlogits[t * E + e] += p[s] * (gs * f[s] - gs * dot);
+      }
+    }
+  }
+  if (lane == 0) wpart[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = 0.0f;
+    for (int w = 0; w < kBalThreads / 64; ++w) v += wpart[w];
+    part[(int64_t)q * gridDim.x + blockIdx.x] = v;
+  }
+}
+
+// seq_loss[q] = alpha / seq_len * (sum of sequence q's partials, in chunk order).
+__global__ void balance_reduce_kernel(int n_chunk, int seq_len, float alpha,
+                                      const float* __restrict__ part, float* __restrict__ seq_loss) {
+  const int q = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  float v = 0.0f;
+  for (int c = 0; c < n_chunk; ++c) v += part[(int64_t)q * n_chunk + c];
+  seq_loss[q] = alpha * (v / (float)seq_len);
+}
+
 __global__ void fill_f32_kernel(float* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -228,14 +329,7 @@ hipError_t launch_route_bwd(const moe_shape_t& s, const float* dtopk_w, const in
                             const float* probs, const uint16_t* x, const float* wg, float* dlogits,
                             float* dw_gate, float* dx_router, hipStream_t st) {
   const bool norm = (s.flags & MOE_NORM_TOPK) != 0;
-  if (s.T == 0) {   // an empty batch: the weight gradient is a sum over no tokens
-    if (dw_gate) {
-      const int64_t n = (int64_t)s.E * s.H;
-      hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                         dw_gate, n);
-    }
-    return hipGetLastError();
-  }
+  if (s.T == 0) return launch_router_grads(s, dlogits, x, wg, dw_gate, dx_router, st);
   const int tpw = (s.T + kWaves - 1) / kWaves;
   const int per_wg = tpw * (kThreads / 64);
   const dim3 grid((unsigned)((s.T + per_wg - 1) / per_wg));
@@ -245,8 +339,23 @@ hipError_t launch_route_bwd(const moe_shape_t& s, const float* dtopk_w, const in
   else
     hipLaunchKernelGGL(route_bwd_kernel<false>, grid, dim3(kThreads), 0, st, s.T, s.E, s.K, tpw,
                        dtopk_w, topk_idx, probs, dlogits);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_router_grads(s, dlogits, x, wg, dw_gate, dx_router, st);
+}
+
+hipError_t launch_router_grads(const moe_shape_t& s, const float* dlogits, const uint16_t* x,
+                               const float* wg, float* dw_gate, float* dx_router, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (s.T == 0) {   // an empty batch: the weight gradient is a sum over no tokens
+    if (dw_gate) {
+      const int64_t n = (int64_t)s.E * s.H;
+      hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                         dw_gate, n);
+      e = hipGetLastError();
+    }
+    return e;
+  }
   if (dw_gate) {
     hipLaunchKernelGGL(router_dwg_kernel, dim3((unsigned)((s.E + 31) / 32), (unsigned)(s.H / 64)),
                        dim3(kDwgThreads), 0, st, s.T, s.H, s.E, dlogits, x, dw_gate);
@@ -265,6 +374,34 @@ hipError_t launch_route_bwd(const moe_shape_t& s, const float* dtopk_w, const in
     e = hipGetLastError();
   }
   return e;
+}
+
+int64_t balance_workspace_floats(int T, int seq_len, int E) {
+  if (seq_len < 1) return 0;
+  // per chunk of each sequence: one partial loss and E selection counts
+  return (int64_t)(T / seq_len) * ((seq_len + kBalTok - 1) / kBalTok) * (1 + E);
+}
+
+hipError_t launch_balance_loss(const moe_shape_t& s, int seq_len, float alpha, const float* probs,
+                               const int32_t* topk_idx, float* seq_loss, float* dlogits, float* ws,
+                               hipStream_t st) {
+  const int n_seq = s.T / seq_len;
+  if (n_seq == 0) return hipSuccess;
+  const int n_chunk = (seq_len + kBalTok - 1) / kBalTok;
+  float* part = ws;
+  int32_t* hc = reinterpret_cast<int32_t*>(ws + (int64_t)n_seq * n_chunk);
+  const dim3 grid((unsigned)n_chunk, (unsigned)n_seq);
+  hipLaunchKernelGGL(balance_hist_kernel, grid, dim3(kThreads), 0, st, seq_len, s.E, s.K, topk_idx,
+                     hc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(balance_kernel, grid, dim3(kBalThreads), 0, st, seq_len, n_seq, s.E, s.K, alpha,
+                     probs, hc, dlogits, part);
+  e = hipGetLastError();
+  if (e != hipSuccess || !seq_loss) return e;
+  hipLaunchKernelGGL(balance_reduce_kernel, dim3((unsigned)n_seq), dim3(64), 0, st, n_chunk,
+                     seq_len, alpha, part, seq_loss);
+  return hipGetLastError();
 }
 
 hipError_t launch_bias_update(const moe_shape_t& s, const int32_t* counts, float gamma, float* bias,

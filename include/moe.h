@@ -229,6 +229,41 @@ moe_status_t moe_route_bwd(const moe_shape_t* shape, const float* dtopk_w, const
                            float* dlogits, float* dw_gate, float* dx_router, void* stream);
 
 /*
+ * moe_router_grads — the router's contractions from a given dlogits [T,E] fp32 (for instance
+ * moe_route_bwd's plus moe_balance_loss's): dw_gate[E,H] = dlogits^T x and dx_router[T,H] =
+ * dlogits w_gate, both fp32 and each optional (dw_gate needs x, 16-byte aligned; dx_router needs
+ * w_gate). With T == 0 dw_gate (if given) is filled with zeros. Layouts as moe_route_bwd.
+ */
+moe_status_t moe_router_grads(const moe_shape_t* shape, const float* dlogits, const uint16_t* x,
+                              const float* w_gate, float* dw_gate, float* dx_router, void* stream);
+
+/*
+ * moe_balance_loss — the sequence-wise balance loss (TR section A2, load-balancing paragraph names
+ * it to keep any one sequence from routing very unevenly; the formula is a reading). The batch is
+ * T / seq_len sequences of seq_len consecutive tokens (seq_len must divide T). In sequence q:
+ *   f_e = E / (K seq_len) * #{(t, j) in q : topk_idx[t, j] = e}      (1 for every e when balanced)
+ *   P_e = (1 / seq_len) * sum_{t in q} probs[t, e]
+ *   seq_loss[q] = alpha * sum_e f_e P_e                               (fp32, device, [T/seq_len])
+ * The batch loss is the mean of seq_loss. Its gradient with respect to the logits (through P and
+ * the softmax; the counts f are piecewise constant) is ADDED to dlogits [T,E] fp32:
+ *   dlogits[t, e] += p_e (g_e - sum_i p_i g_i),  g = alpha f / (seq_len * T / seq_len).
+ * Either output may be NULL, not both. probs [T,E] fp32 and topk_idx [T,K] int32 are moe_route's
+ * outputs; experts outside 0..E-1 in topk_idx are not counted. alpha must be finite and >= 0.
+ * ws (device, caller-owned, ws_bytes >= moe_balance_workspace_size) holds per-chunk counts and
+ * partial sums; the loss
+ * is summed in a fixed order, so it is deterministic.
+ * Errors: MOE_ERR_INVALID_ARG for a bad seq_len, alpha or pointer; MOE_ERR_WORKSPACE for a small
+ * ws. T == 0 is a no-op.
+ */
+moe_status_t moe_balance_loss(const moe_shape_t* shape, int32_t seq_len, float alpha,
+                              const float* probs, const int32_t* topk_idx, float* seq_loss,
+                              float* dlogits, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of scratch `ws` that moe_balance_loss needs (per 256-token chunk of each sequence: a
+ * partial sum of the loss and E selection counts); 0 for an invalid shape or seq_len. */
+size_t moe_balance_workspace_size(const moe_shape_t* shape, int32_t seq_len);
+
+/*
  * moe_bias_update — one step of the aux-loss-free load balancing (TR section A2, load-balancing
  * paragraph: the per-expert bias is adjusted during training to keep the loads balanced; the
  * rule is a reading): with the mean load T*K/E,

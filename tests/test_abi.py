@@ -128,6 +128,35 @@ def test_router_backward_and_bias_update_checks(lib):
         assert "gamma" in M.moe_last_error()
 
 
+def test_balance_loss_and_router_grads_checks(lib):
+    s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
+    d = ctypes.c_void_p(16)
+    f = ctypes.c_float
+    need = M.moe_balance_workspace_size(s, 4)
+    assert need == 4 * 2 * (1 + 8)                        # two sequences of one chunk each
+    assert M.moe_balance_workspace_size(s, 3) == 0        # 3 does not divide 8
+    ok = (d, d, d, d, d, need)
+
+    def call(shape, seq_len, alpha, *args):
+        return lib.moe_balance_loss(ctypes.byref(shape), seq_len, f(alpha), *args, None)
+
+    assert call(s, 3, 0.1, *ok) == -1
+    assert call(s, 0, 0.1, *ok) == -1
+    assert call(s, 4, -1.0, *ok) == -1
+    assert call(s, 4, float("nan"), *ok) == -1
+    assert call(s, 4, 0.1, d, d, None, None, d, need) == -1      # nothing to compute
+    assert call(s, 4, 0.1, None, d, d, None, d, need) == -1      # probs
+    assert call(s, 4, 0.1, d, None, None, d, d, need) == -1      # topk_idx
+    assert call(s, 4, 0.1, d, d, d, None, None, need) == -1      # ws
+    assert call(s, 4, 0.1, d, d, d, None, d, need - 1) == -3     # ws too small
+    s0 = M.make_shape(0, 256, 8, 2, 128, 1, 16)
+    assert call(s0, 4, 0.1, None, None, d, None, None, 0) == 0
+    assert lib.moe_router_grads(ctypes.byref(s), None, d, d, d, d, None) == -1
+    assert lib.moe_router_grads(ctypes.byref(s), d, None, d, d, None, None) == -1
+    assert lib.moe_router_grads(ctypes.byref(s), d, d, None, None, d, None) == -1
+    assert lib.moe_router_grads(ctypes.byref(s), d, ctypes.c_void_p(18), d, d, None, None) == -1
+
+
 def test_fp32_wgrad_checks(lib):
     s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
     d, odd = ctypes.c_void_p(16), ctypes.c_void_p(24)

@@ -6,7 +6,10 @@ Bars, derived from fp32 arithmetic (u = 2^-24), against the float64 oracle round
   * dWg = dlogits^T x (n = T/4 + 8 sequential fp32 additions per wavefront, then four partial sums)
     and dx_router = dlogits Wg (n = E + 4): |got - ref| <= n u sum_k |a_k b_k| + u |ref|, plus the
     dlogits bound carried through the product; and rel-L2 <= 1e-5;
-  * bias update: bit-exact (integer comparison and one fp32 add on both sides).
+  * bias update: bit-exact (integer comparison and one fp32 add on both sides);
+  * balance loss: per sequence within (seq_len + E + 8) u of the oracle (all terms non-negative;
+    partial sums per 256-token chunk, reduced in chunk order);
+    its gradient as stated at the test.
 Inputs come from the seeded generators and the oracle's own routing, never from the GPU.
 """
 import numpy as np
@@ -123,3 +126,54 @@ def test_bias_update_bitexact(T, K, E):
         torch.cuda.synchronize()
         ref = O.bias_update(b, counts, T, K, gamma)
         assert np.array_equal(_np(b_d).view(np.uint32), ref.view(np.uint32)), gamma
+
+
+@pytest.mark.parametrize("T,E,K,seq_len", [(64, 8, 2, 16), (300, 20, 4, 100), (8192, 128, 6, 4096),
+                                           (8192, 128, 6, 1024), (257, 256, 8, 257)])
+def test_balance_loss_parity(T, E, K, seq_len):
+    """Loss: every term f_e P_e is >= 0, so fp32 sums of n terms are within n u of the result.
+    Gradient (added to an existing dlogits): |got - ref| <= 2 u |ref| + (E + 8) u p_e (g_e + sum_i
+    p_i g_i), all of those terms non-negative."""
+    log(f"balance loss T={T} E={E} K={K} seq_len={seq_len}")
+    rng = np.random.default_rng(T + E + seq_len)
+    p = O.softmax_probs(draw_logits(T, E, seed=T + 3))
+    idx, _ = O.select_topk(p, None, K)
+    base = rng.standard_normal((T, E)).astype(np.float32) * np.float32(1e-4)
+    alpha = 1e-3
+    s = M.make_shape(T, 128, E, K, 128, 0, 16)
+    loss_d = torch.empty(T // seq_len, device=DEV)
+    dz_d = f32_dev(base)
+    ws = torch.empty(M.moe_balance_workspace_size(s, seq_len) // 4, device=DEV)
+    M.moe_balance_loss(s, seq_len, alpha, f32_dev(p), i32_dev(idx), loss_d, dz_d, ws)
+    torch.cuda.synchronize()
+    ref_loss, ref_dz = O.balance_loss(p, idx, seq_len, alpha)
+    got_loss = _np(loss_d).astype(np.float64)
+    assert np.all(np.abs(got_loss - ref_loss) <= (seq_len + E + 8) * U * np.abs(ref_loss)), \
+        (got_loss, ref_loss)
+    ref = base.astype(np.float64) + ref_dz
+    n_seq = T // seq_len
+    pv = p.astype(np.float64)
+    g = np.zeros((T, E))
+    for q in range(n_seq):
+        f = np.bincount(idx[q * seq_len:(q + 1) * seq_len].reshape(-1), minlength=E) * (E / (K * seq_len))
+        g[q * seq_len:(q + 1) * seq_len] = alpha * f / (seq_len * n_seq)
+    bound = 2 * U * np.abs(ref) + (E + 8) * U * pv * (g + (pv * g).sum(axis=1, keepdims=True))
+    err = np.abs(_np(dz_d).astype(np.float64) - ref)
+    assert np.all(err <= bound), float((err - bound).max())
+    log(f"  loss {got_loss[:4]}, worst err/bound {float((err / bound).max()):.3f}")
+
+
+def test_router_grads_from_given_dlogits():
+    T, H, E, K = 512, 256, 32, 4
+    p, idx, dw, x, wg = _inputs(T, H, E, K, seed=11)
+    dz = O.route_backward(p, idx, dw) + O.balance_loss(p, idx, 128, 1e-2)[1].astype(np.float32)
+    dz = dz.astype(np.float32)
+    s = M.make_shape(T, H, E, K, 128, 0, 16)
+    dwg_d, dx_d = torch.empty(E, H, device=DEV), torch.empty(T, H, device=DEV)
+    M.moe_router_grads(s, f32_dev(dz), bf16_dev(x), f32_dev(wg), dwg_d, dx_d)
+    torch.cuda.synchronize()
+    xv, adz, awg = O.bf16_to_f64(x), np.abs(dz.astype(np.float64)), np.abs(wg.astype(np.float64))
+    ref = O.router_weight_grad(dz, x)
+    _check_contraction(_np(dwg_d), ref, (T / 4 + 8) * U * (adz.T @ np.abs(xv)) + U * np.abs(ref), "dWg")
+    ref = O.router_input_grad(dz, wg)
+    _check_contraction(_np(dx_d), ref, (E + 4) * U * (adz @ awg) + U * np.abs(ref), "dx_router")
