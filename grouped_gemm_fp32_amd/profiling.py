@@ -26,11 +26,35 @@ import sys
 STAGE_OF = {
     "ggemm_tall8_kernel<0>": "fwd_gateup", "ggemm_tall8_kernel<1>": "fwd_down",
     "ggemm_tall8_kernel<2>": "dgrad_down", "ggemm_tall8_kernel<3>": "dgrad_gateup",
-    "ggemm_wgrad8_kernel<4>": "wgrad_down", "ggemm_wgrad8_kernel<5>": "wgrad_gateup",
+    "ggemm_wgrad8_kernel<4,false>": "wgrad_down", "ggemm_wgrad8_kernel<5,false>": "wgrad_gateup",
     "gather_rows_kernel": "permute", "gather_sum_kernel<true>": "combine",
     "combine_bwd_kernel": "combine_bwd", "gather_sum_kernel<false>": "unpermute_bwd",
     "route_kernel<1>": "route",
 }
+
+
+# Kernels the benchmark times outside the step (extra measurements and context).
+OUTSIDE_STEP = {
+    "ggemm_wgrad8_kernel<4,true>": "fp32-dW wgrad down (outside the step)",
+    "ggemm_wgrad8_kernel<5,true>": "fp32-dW wgrad gate/up (outside the step)",
+    "route_bwd_kernel<true>": "router backward (outside the step)",
+    "router_dwg_kernel": "router backward (outside the step)",
+    "router_dx_kernel": "router backward (outside the step)",
+    "balance_hist_kernel": "balance loss (outside the step)",
+    "balance_kernel": "balance loss (outside the step)",
+    "balance_reduce_kernel": "balance loss (outside the step)",
+    "bias_update_kernel": "bias update (outside the step)",
+}
+
+
+def label(k: str) -> str:
+    if k in STAGE_OF:
+        return STAGE_OF[k]
+    if k in OUTSIDE_STEP:
+        return OUTSIDE_STEP[k]
+    if k.startswith("Cijk_"):
+        return "library GEMM reference (outside the step)"
+    return ""
 
 
 def short_name(n: str) -> str:
@@ -54,7 +78,7 @@ def stats_table(path: str) -> str:
     out = ["| kernel | stage | calls | avg (us) | total (ms) | share |", "|---|---|---|---|---|---|"]
     for r in rows:
         k = short_name(r["Name"])
-        out.append(f"| {k} | {STAGE_OF.get(k, '')} | {r['Calls']} | "
+        out.append(f"| {k} | {label(k)} | {r['Calls']} | "
                    f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
                    f"{float(r['Percentage']):.1f}% |")
     return "\n".join(out)
@@ -74,8 +98,13 @@ def counter_means(path: str) -> dict:
 def traffic(fetch_dir: str, write_dir: str, calib_mib: float) -> dict:
     known = calib_mib * 2 ** 20
     fr, wr = counter_rows(fetch_dir), counter_rows(write_dir)
-    foreign = [r for r in fr if "moe::" not in r["Kernel_Name"]]
-    cal = max(foreign, key=lambda r: float(r["Counter_Value"]))
+    # The calibration copy is the first kernel outside this library that reads at least a quarter
+    # of its size (the fills that prepare it read nothing; library GEMMs timed later come after).
+    foreign = [r for r in fr if "moe::" not in r["Kernel_Name"]
+               and float(r["Counter_Value"]) * 1024.0 >= known / 4]
+    if not foreign:
+        raise ValueError("no calibration copy found in the FETCH_SIZE run")
+    cal = min(foreign, key=lambda r: int(r["Dispatch_Id"]))
     cal_w = [r for r in wr if r["Dispatch_Id"] == cal["Dispatch_Id"]]
     if not cal_w or cal_w[0]["Kernel_Name"] != cal["Kernel_Name"]:
         raise ValueError("the FETCH_SIZE and WRITE_SIZE runs do not line up by dispatch id")
