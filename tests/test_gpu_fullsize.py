@@ -7,7 +7,7 @@ import torch
 
 import grouped_gemm_fp32_amd as M
 from oracle import moe_oracle as O
-from synth import (get_config, draw_x, draw_wg, draw_sel_bias, draw_logit_bias, draw_w1_all,
+from synth import (get_config, draw_probs, draw_x, draw_wg, draw_sel_bias, draw_logit_bias, draw_w1_all,
                    draw_w2_all, draw_dy, uniform_topk, uniform_logits)
 from tests.gpu_helpers import (DEV, log, bf16_dev, f32_dev, i32_dev, bits_host, vals_host, rel_l2,
                                assert_bf16_close)
@@ -289,3 +289,57 @@ def test_decode_256_tokens_full_layer(name):
     assert_bf16_close(vals_host(buf["a"])[:total], ref["a"], "a")
     assert_bf16_close(vals_host(buf["y_perm"])[:total], ref["y_perm"], "y_perm")
     assert_bf16_close(vals_host(buf["y"]), ref["y"], "y")
+
+
+def test_largest_shape_routing_permutation_and_forward():
+    """The largest shape the library accepts in tokens, experts, slots and shared experts: T=262144,
+    E=256, K=8, S=4, block 256 (hidden 128, intermediate 64 to keep it small). Routing from given
+    probabilities and every integer map bit-exact; sampled rows through the expert FFN and sampled
+    tokens through the combine."""
+    cfg = get_config("c1", T=262144, H=128, E=256, K=8, I=64, S=4, block_m=256, seed=3)
+    log(f"largest shape: {cfg}")
+    s = M.make_shape(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.S, cfg.block_m,
+                     M.MOE_NORM_TOPK | M.MOE_PROBS_IN)
+    p = draw_probs(cfg.T, cfg.E, seed=3, levels=6)   # many ties: the index order decides them
+    sb = (np.random.default_rng(3).integers(-3, 4, cfg.E) / 1024).astype(np.float32)
+    x, w1, w2 = draw_x(cfg), draw_w1_all(cfg), draw_w2_all(cfg)
+    X, W1, W2 = bf16_dev(x), bf16_dev(w1), bf16_dev(w2)
+    buf = M.alloc_buffers(s, DEV)
+    buf["probs"].copy_(f32_dev(p))
+    M.moe_route(s, None, None, None, f32_dev(sb), None, buf["probs"], buf["topk_idx"], buf["topk_w"],
+                buf["expert_counts"])
+    M.moe_permute(s, buf["topk_idx"], X, buf["seg_offsets"], buf["tile_group"], buf["total_rows"],
+                  buf["row_token"], buf["pos"], buf["x_perm"], buf["ws"])
+    M.grouped_gemm_fwd(s, M.MOE_FWD, buf["x_perm"], buf["seg_offsets"], buf["tile_group"],
+                       buf["total_rows"], W1, W2, buf["h_save"], buf["a"], buf["y_perm"])
+    M.moe_combine(s, buf["y_perm"], buf["pos"], buf["topk_w"], buf["seg_offsets"], buf["y"])
+    torch.cuda.synchronize()
+    idx, w = O.select_topk(p, sb, cfg.K)
+    np.testing.assert_array_equal(_np(buf["topk_idx"]), idx)
+    np.testing.assert_array_equal(_np(buf["expert_counts"]), O.expert_counts(idx, cfg.E))
+    np.testing.assert_allclose(_np(buf["topk_w"]), w, rtol=0, atol=1e-6)
+    seg, rt, pos, total = _check_maps_exact(buf, idx, cfg)
+    rng = np.random.default_rng(4)
+    rows = _sample_rows(seg, rng, per_group=3, groups=40)
+    R = torch.from_numpy(rows).to(DEV)
+    ok = rt[rows] >= 0
+    got_x = bits_host(buf["x_perm"][R])
+    assert np.array_equal(got_x[ok], x[rt[rows][ok]]) and not got_x[~ok].any()
+    h_ref, a_ref, y_ref = _oracle_rows(rows, seg, rt, x, cfg, lambda g: w1[g], lambda g: w2[g])
+    assert_bf16_close(vals_host(buf["h_save"][R]), O.round_bf16(h_ref), "h_save rows")
+    assert_bf16_close(vals_host(buf["a"][R]), a_ref, "a rows")
+    assert_bf16_close(vals_host(buf["y_perm"][R]), y_ref, "y_perm rows")
+    toks = np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 14, replace=False)])
+    y_tok = np.zeros((len(toks), cfg.H))
+    for i, t in enumerate(toks):
+        xt = O.bf16_to_f64(x[t:t + 1])
+        for j in range(cfg.K):
+            e = idx[t, j]
+            y_tok[i] += np.float64(w[t, j]) * O.round_bf16(
+                O.expert_ffn_rows(xt, O.bf16_to_f64(w1[e]), O.bf16_to_f64(w2[e]), cfg.I)[2][0])
+        for sh in range(cfg.S):
+            g = cfg.E + sh
+            y_tok[i] += O.round_bf16(
+                O.expert_ffn_rows(xt, O.bf16_to_f64(w1[g]), O.bf16_to_f64(w2[g]), cfg.I)[2][0])
+    assert_bf16_close(vals_host(buf["y"][torch.from_numpy(toks).to(DEV)]), O.round_bf16(y_tok),
+                      "y tokens")
