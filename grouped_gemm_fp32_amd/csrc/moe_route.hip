@@ -9,8 +9,8 @@
 //      bf16, so exact; each fp32 weight is split exactly into three bf16 parts w = hi + mid + lo
 //      (24 significand bits), and three v_mfma_f32_32x32x16_bf16 per k-slice accumulate x*hi +
 //      x*mid + x*lo in fp32. Every product is exact in fp32, so this is the fp32 dot product up
-//      to summation order. One workgroup per 32 tokens x 32 experts; its four wavefronts take
-//      every fourth 64-k step and their partial sums are added in wavefront order (deterministic).
+//      to summation order. One workgroup per 64 tokens (32 for small batches) x 32 experts; its
+//      wavefronts split the 64-k steps and their partial sums are added in wavefront order.
 //   2. route_kernel, one wavefront per token at a time (a few consecutive tokens each): softmax
 //      over E, key = p + b, K rounds of a wave-wide arg-max on a 64-bit (key, index) code,
 //      weights, per-expert counts (an LDS histogram per workgroup, then one atomic per expert).
@@ -37,7 +37,8 @@ __device__ __forceinline__ uint32_t key_code(float k) {
 }
 
 // ---- 1. router logits ---------------------------------------------------------------------------
-constexpr int kLgTile = 32;   // tokens and experts per workgroup (the MFMA's 32 x 32)
+constexpr int kLgTile = 32;      // experts per workgroup (the MFMA's 32)
+constexpr int kLgLargeT = 4096;  // from this many tokens the logits use two token blocks per wave
 
 // Exact split of 8 fp32 values into three bf16 vectors with hi + mid + lo == w (each part is the
 // remainder rounded to bf16, so every subtraction is exact in fp32).
@@ -56,48 +57,83 @@ __device__ __forceinline__ void split3(const float4& w0, const float4& w1, bf16x
   }
 }
 
-// logits[t0.., e0..] for a 32 x 32 tile. Lanes 0-31 hold token (A) and expert (B) rows r = lane;
-// within a 64-k step lane half h = lane >> 5 covers k = 32 h + 8 s .. +8 in slice s (the same
-// assignment for both operands, so each MFMA sums matching pairs and four slices cover the step).
-__global__ __launch_bounds__(kRouteThreads) void router_logits_kernel(
+// logits[t0.., e0..] for TB x 32 tokens and 32 experts. Lanes 0-31 hold token (B) and expert (A)
+// rows r = lane; within a 64-k step lane half h = lane >> 5 covers k = 32 h + 8 s .. +8 in slice s
+// (the same assignment for both operands, so each MFMA sums matching pairs and four slices cover
+// the step). With TB = 2 token blocks every split of Wg feeds two MFMA blocks. Each wavefront
+// takes every NW-th 64-k step and loads the next one's operands while the current MFMAs run; the
+// NW partial sums are added in wavefront order (deterministic). Large batches use TB = 2 and four
+// wavefronts; small ones (decode) one token block and eight, to spread the contraction wider.
+template <int TB>
+struct LgOps {
+  uint4 x[TB][4];   // token blocks: 4 slices of 8 bf16
+  float4 w[8];      // the expert row: 4 slices of 8 fp32
+};
+
+template <int TB, int NW>
+__global__ __launch_bounds__(NW * 64) void router_logits_kernel(
     int T, int H, int E, const uint16_t* __restrict__ x, const float* __restrict__ wg,
     const float* __restrict__ logit_bias, float* __restrict__ logits) {
-  __shared__ float red[4][kLgTile][kLgTile + 1];
+  constexpr int TOK = 32 * TB;
+  __shared__ float red[NW][kLgTile][TOK + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * kLgTile, e0 = blockIdx.y * kLgTile;
+  const int t0 = blockIdx.x * TOK, e0 = blockIdx.y * kLgTile;
   const int r = lane & 31, h = lane >> 5;
-  const int t = min(t0 + r, T - 1), e = min(e0 + r, E - 1);   // rows past the end: not stored
-  const uint16_t* xr = x + (int64_t)t * H + h * 32;
-  const float* wr = wg + (int64_t)e * H + h * 32;
-  f32x16_t acc;
+  // rows past the end are clamped (read, never stored)
+  const uint16_t* xr[TB];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
-  for (int step = wave; step < H / 64; step += 4) {   // H % 64 == 0
+  for (int b = 0; b < TB; ++b) xr[b] = x + (int64_t)min(t0 + 32 * b + r, T - 1) * H + h * 32;
+  const float* wr = wg + (int64_t)min(e0 + r, E - 1) * H + h * 32;
+  auto load = [&](int step, LgOps<TB>& o) {
     const int k = step * 64;
-    uint4 xa[4];
-    float4 wa[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const uint4*>(xr + k + 8 * i);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wa[i] = *reinterpret_cast<const float4*>(wr + k + 4 * i);
+      for (int b = 0; b < TB; ++b) o.x[b][i] = *reinterpret_cast<const uint4*>(xr[b] + k + 8 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.w[i] = *reinterpret_cast<const float4*>(wr + k + 4 * i);
+  };
+  f32x16_t acc[TB];
+#pragma unroll
+  for (int b = 0; b < TB; ++b)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[b][q] = 0.0f;
+  const int nstep = H / 64;   // H % 64 == 0
+  LgOps<TB> cur;
+  if (wave < nstep) load(wave, cur);
+  for (int step = wave; step < nstep; step += NW) {
+    LgOps<TB> nxt;
+    if (step + NW < nstep) load(step + NW, nxt);
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
-      bf16x8_t a, whi, wmid, wlo;
-      __builtin_memcpy(&a, &xa[sl], 16);
-      split3(wa[2 * sl], wa[2 * sl + 1], whi, wmid, wlo);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wlo, a, acc, 0, 0, 0);   // smallest first
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wmid, a, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(whi, a, acc, 0, 0, 0);
-    }
-  }
-  // D[expert][token]: lane -> token r, register q -> expert 8 (q / 4) + 4 h + q % 4.
+      bf16x8_t a[TB], whi, wmid, wlo;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) red[wave][8 * (q >> 2) + 4 * h + (q & 3)][r] = acc[q];
+      for (int b = 0; b < TB; ++b) __builtin_memcpy(&a[b], &cur.x[b][sl], 16);
+      split3(cur.w[2 * sl], cur.w[2 * sl + 1], whi, wmid, wlo);
+#pragma unroll
+      for (int b = 0; b < TB; ++b)   // smallest part first
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wlo, a[b], acc[b], 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wmid, a[b], acc[b], 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(whi, a[b], acc[b], 0, 0, 0);
+    }
+    cur = nxt;
+  }
+  // D[expert][token]: lane -> token 32 b + r, register q -> expert 8 (q / 4) + 4 h + q % 4.
+#pragma unroll
+  for (int b = 0; b < TB; ++b)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) red[wave][8 * (q >> 2) + 4 * h + (q & 3)][32 * b + r] = acc[b][q];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < kLgTile * kLgTile; idx += kRouteThreads) {
-    const int el = idx / kLgTile, tl = idx % kLgTile;
+  for (int idx = threadIdx.x; idx < kLgTile * TOK; idx += NW * 64) {
+    const int el = idx / TOK, tl = idx % TOK;
     if (t0 + tl < T && e0 + el < E) {
-      float z = red[0][el][tl] + red[1][el][tl] + red[2][el][tl] + red[3][el][tl];
+      float z = red[0][el][tl];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) z += red[w][el][tl];
       if (logit_bias) z += logit_bias[e0 + el];
       logits[(int64_t)(t0 + tl) * E + e0 + el] = z;
     }
@@ -299,9 +335,13 @@ hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg
     return hipGetLastError();
   }
   if (x) {
-    const dim3 lg((unsigned)((s.T + kLgTile - 1) / kLgTile), (unsigned)((s.E + kLgTile - 1) / kLgTile));
-    hipLaunchKernelGGL(router_logits_kernel, lg, block, 0, st, s.T, s.H, s.E, x, wg, logit_bias,
-                       logits);
+    const unsigned ge = (unsigned)((s.E + kLgTile - 1) / kLgTile);
+    if (s.T >= kLgLargeT)
+      hipLaunchKernelGGL((router_logits_kernel<2, 4>), dim3((unsigned)((s.T + 63) / 64), ge), dim3(256),
+                         0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
+    else
+      hipLaunchKernelGGL((router_logits_kernel<1, 8>), dim3((unsigned)((s.T + 31) / 32), ge),
+                         dim3(512), 0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
