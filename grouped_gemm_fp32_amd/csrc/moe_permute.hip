@@ -162,6 +162,8 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
 }
 
 // One wavefront per row: x_perm[r] = x[row_token[r]] (or 0), 16 B per lane per step.
+constexpr int kGatherU = 8;   // 16-byte chunks per lane per batch (a 4096-wide row in one batch)
+
 __global__ __launch_bounds__(kThreads) void gather_rows_kernel(int H, int64_t mcap,
                                                                const int32_t* __restrict__ total,
                                                                const int32_t* __restrict__ row_token,
@@ -176,8 +178,22 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(int H, int64_t mc
   if (t < 0) {
     for (int c = lane; c < nv; c += 64) dst[c] = make_uint4(0, 0, 0, 0);
   } else {
+    // all of a batch's loads are issued before its stores, so a wavefront keeps kGatherU 16-byte
+    // loads in flight instead of one
     const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * H);
-    for (int c = lane; c < nv; c += 64) dst[c] = src[c];
+    for (int c0 = lane; c0 < nv; c0 += 64 * kGatherU) {
+      uint4 v[kGatherU];
+#pragma unroll
+      for (int u = 0; u < kGatherU; ++u) {
+        const int c = c0 + 64 * u;
+        v[u] = c < nv ? src[c] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kGatherU; ++u) {
+        const int c = c0 + 64 * u;
+        if (c < nv) dst[c] = v[u];
+      }
+    }
   }
 }
 
