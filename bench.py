@@ -339,6 +339,17 @@ def main():
                           for k in per_row},
         "experts_touched": touched,
     }
+    # The forward, data-gradient and weight-gradient passes, each its two grouped GEMMs.
+    passes = {"fwd": ("fwd_gateup", "fwd_down"), "dx": ("dgrad_down", "dgrad_gateup"),
+              "dw": ("wgrad_down", "wgrad_gateup")}
+    out["passes"] = {}
+    for name, ks in passes.items():
+        if not all(k in per_row for k in ks):
+            continue
+        t = sum(stage_ms[k] for k in ks)
+        tf = sum(per_row[k] for k in ks) * rows / (t * 1e-3) / 1e12
+        out["passes"][name] = {"ms": round(t, 4), "tflops": round(tf, 1),
+                               "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
     if router_bwd is not None:
         out["router_backward"] = router_bwd
     if args.workload == "c2":

@@ -3,6 +3,7 @@
     python -m grouped_gemm_fp32_amd.profiling stats <kernel_stats.csv>
     python -m grouped_gemm_fp32_amd.profiling traffic <fetch_dir> <write_dir> --calib-mib N \
         [--workload NAME] [--json OUT]
+    python -m grouped_gemm_fp32_amd.profiling mfma <counter_dir>
 
 `stats` prints the per-kernel table (calls, average and total duration, share of GPU time).
 `traffic` reads two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (KiB per dispatch) of
@@ -10,6 +11,10 @@ the same deterministic program, scales each counter by what it reads for a plain
 size in the same run (the dispatch with the largest FETCH_SIZE outside this library: bench.py's
 `--calib-copy-mib` elementwise copy of a cold buffer, `calib` MiB read and written; the same
 dispatch id in the WRITE_SIZE run), and reports HBM bytes per launch.
+`mfma` reads one `rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE` run and
+reports, per kernel, the matrix instructions per launch, the fraction of SIMD cycles the matrix
+unit was busy, and the shader clock the launch ran at (GRBM_GUI_ACTIVE sums the busy cycles of
+every XCD; dividing by the XCD count and by the dispatch's duration gives the clock).
 """
 from __future__ import annotations
 
@@ -129,11 +134,55 @@ def traffic(fetch_dir: str, write_dir: str, calib_mib: float) -> dict:
     return out
 
 
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU.
+N_XCD, N_SIMD = 8, 256 * 4
+
+
+def mfma_util(path: str) -> dict:
+    """Per kernel: mean over its dispatches of the MFMA-busy fraction of all SIMD cycles, the
+    shader clock (GHz), the duration (us), MFMA instructions per launch and busy cycles per
+    instruction. Dispatches that lack one of the three counters are skipped."""
+    disp = collections.defaultdict(dict)
+    for r in counter_rows(path):
+        key = (short_name(r["Kernel_Name"]), int(r["Dispatch_Id"]))
+        d = disp[key]
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    per = collections.defaultdict(list)
+    need = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+    for (k, _), d in disp.items():
+        if not all(n in d for n in need) or d["SQ_INSTS_MFMA"] <= 0 or d["_ns"] <= 0:
+            continue
+        cyc = d["GRBM_GUI_ACTIVE"] / N_XCD
+        per[k].append({"busy_frac": d["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc),
+                       "clock_ghz": cyc / d["_ns"],
+                       "us": d["_ns"] / 1e3,
+                       "mfma_insts": d["SQ_INSTS_MFMA"],
+                       "cycles_per_inst": d["SQ_VALU_MFMA_BUSY_CYCLES"] / d["SQ_INSTS_MFMA"]})
+    out = {}
+    for k, v in per.items():
+        out[k] = {f: sum(e[f] for e in v) / len(v) for f in v[0]}
+        out[k]["dispatches"] = len(v)
+    return out
+
+
+def mfma_table(path: str) -> str:
+    rows = ["| kernel | stage | dispatches | avg (us) | MFMA instr / launch | busy cycles / instr "
+            "| clock (GHz) | MFMA busy (of SIMD cycles) |", "|---|---|---|---|---|---|---|---|"]
+    for k, e in sorted(mfma_util(path).items(), key=lambda kv: -kv[1]["us"]):
+        rows.append(f"| {k} | {label(k)} | {e['dispatches']} | {e['us']:.1f} | "
+                    f"{e['mfma_insts']:.0f} | {e['cycles_per_inst']:.1f} | {e['clock_ghz']:.2f} | "
+                    f"{100 * e['busy_frac']:.1f}% |")
+    return "\n".join(rows)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
     t = sub.add_parser("traffic")
     t.add_argument("fetch")
     t.add_argument("write")
@@ -144,6 +193,9 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.csv))
+        return
+    if a.cmd == "mfma":
+        print(mfma_table(a.dir))
         return
     tr = traffic(a.fetch, a.write, a.calib_mib)
     print(json.dumps(tr, indent=1))
