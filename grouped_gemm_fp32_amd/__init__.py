@@ -184,7 +184,7 @@ def moe_workspace_size(shape: MoeShape) -> int:
 def moe_route(shape, x, w_gate, logit_bias, sel_bias, logits, probs, topk_idx, topk_w,
               expert_counts, stream=None):
     lib = load_library()
-    st = _stream(stream, topk_idx)
+    st = _stream(stream, topk_idx, expert_counts)
     _check("moe_route", lib.moe_route(
         ctypes.byref(shape), _ptr(x, "x", _bf16()), _ptr(w_gate, "w_gate", _f32()),
         _ptr(logit_bias, "logit_bias", _f32()), _ptr(sel_bias, "sel_bias", _f32()),

@@ -66,8 +66,8 @@ int64_t capacity(const moe_shape_t* s) {
     }                                                             \
   } while (0)
 
-// A bf16 tensor the grouped GEMMs read or write: non-NULL and 16-byte aligned (the kernels move
-// 16-byte chunks).
+// A bf16 activation or weight tensor: non-NULL and 16-byte aligned (every kernel that reads or
+// writes one moves 16-byte chunks).
 #define REQUIRE_T(p)                                                   \
   do {                                                                 \
     REQUIRE(p);                                                        \
@@ -117,7 +117,12 @@ moe_status_t moe_route(const moe_shape_t* s, const uint16_t* x, const float* w_g
                        const float* logit_bias, const float* sel_bias, float* logits, float* probs,
                        int32_t* topk_idx, float* topk_w, int32_t* expert_counts, void* stream) {
   CHECK_SHAPE(s);
-  if (s->T == 0) return MOE_OK;
+  if (s->T == 0) {
+    // no token routed: every expert's count is zero
+    if (!expert_counts) return MOE_OK;
+    return hip_status(moe::launch_fill_i32(expert_counts, 0, s->E, (hipStream_t)stream),
+                      "moe_route");
+  }
   REQUIRE(topk_idx);
   REQUIRE(topk_w);
   if (s->flags & MOE_PROBS_IN) {
@@ -152,7 +157,10 @@ moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx, const ui
   REQUIRE(tile_group);
   REQUIRE(row_token);
   REQUIRE(pos);
-  if (x) REQUIRE(x_perm);
+  if (x) {
+    REQUIRE_T(x);
+    REQUIRE_T(x_perm);
+  }
   REQUIRE(ws);
   if (ws_bytes < moe_workspace_size(s)) {
     set_err("workspace smaller than moe_workspace_size()");
@@ -285,12 +293,11 @@ moe_status_t moe_combine(const moe_shape_t* s, const uint16_t* y_perm, const int
                          void* stream) {
   CHECK_SHAPE(s);
   if (s->T == 0) return MOE_OK;
-  REQUIRE(y_perm);
+  REQUIRE_T(y_perm);
   REQUIRE(pos);
   REQUIRE(topk_w);
   REQUIRE(seg_offsets);
-  REQUIRE(y);
-  if (s->T == 0) return MOE_OK;
+  REQUIRE_T(y);
   return hip_status(moe::launch_combine(*s, y_perm, pos, topk_w, seg_offsets, y,
                                         (hipStream_t)stream),
                     "moe_combine");
@@ -302,16 +309,15 @@ moe_status_t moe_combine_bwd(const moe_shape_t* s, const uint16_t* dy, const uin
                              uint16_t* dy_perm, float* dtopk_w, void* stream) {
   CHECK_SHAPE(s);
   if (s->T == 0) return MOE_OK;
-  REQUIRE(dy);
-  REQUIRE(y_perm);
+  REQUIRE_T(dy);
+  REQUIRE_T(y_perm);
   REQUIRE(pos);
   REQUIRE(topk_w);
   REQUIRE(seg_offsets);
   REQUIRE(row_token);
   REQUIRE(total_rows);
-  REQUIRE(dy_perm);
+  REQUIRE_T(dy_perm);
   REQUIRE(dtopk_w);
-  if (s->T == 0) return MOE_OK;
   return hip_status(moe::launch_combine_bwd(*s, capacity(s), dy, y_perm, pos, topk_w, seg_offsets,
                                             row_token, total_rows, dy_perm, dtopk_w,
                                             (hipStream_t)stream),
@@ -322,11 +328,10 @@ moe_status_t moe_unpermute_bwd(const moe_shape_t* s, const uint16_t* dx_perm, co
                                const int32_t* seg_offsets, uint16_t* dx, void* stream) {
   CHECK_SHAPE(s);
   if (s->T == 0) return MOE_OK;
-  REQUIRE(dx_perm);
+  REQUIRE_T(dx_perm);
   REQUIRE(pos);
   REQUIRE(seg_offsets);
-  REQUIRE(dx);
-  if (s->T == 0) return MOE_OK;
+  REQUIRE_T(dx);
   return hip_status(moe::launch_unpermute_bwd(*s, dx_perm, pos, seg_offsets, dx,
                                               (hipStream_t)stream),
                     "moe_unpermute_bwd");

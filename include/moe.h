@@ -20,12 +20,13 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream) and never
  *     synchronises the host. Data-dependent sizes (total_rows, tile_group) stay on the device.
  *   - Arguments are checked on the host before any launch: MOE_ERR_INVALID_ARG for a NULL
- *     required pointer, a bf16 tensor of grouped_gemm_fwd/bwd that is not 16-byte aligned, or an
- *     impossible shape, MOE_ERR_UNSUPPORTED for shapes the kernels are not built for,
- *     MOE_ERR_WORKSPACE if ws_bytes is too small.
- *   - T == 0 (an empty batch) reads nothing: moe_permute writes seg_offsets = 0 and
- *     total_rows = 0, grouped_gemm_bwd with a WGRAD bit writes zero weight gradients, every other
- *     call is a no-op returning MOE_OK; pointers to T- or Mcap-sized arrays may then be NULL.
+ *     required pointer, a bf16 activation or weight tensor that is not 16-byte aligned (every
+ *     kernel moves them in 16-byte chunks), or an impossible shape, MOE_ERR_UNSUPPORTED for
+ *     shapes the kernels are not built for, MOE_ERR_WORKSPACE if ws_bytes is too small.
+ *   - T == 0 (an empty batch) reads nothing: moe_route writes expert_counts = 0 (if given),
+ *     moe_permute writes seg_offsets = 0 and total_rows = 0, grouped_gemm_bwd with a WGRAD bit
+ *     writes zero weight gradients, every other call is a no-op returning MOE_OK; pointers to
+ *     T- or Mcap-sized arrays may then be NULL.
  *     A failed launch returns MOE_ERR_HIP; moe_last_error() then describes it.
  *   - Notation: T tokens, H hidden, E routed experts, K experts per token, I expert intermediate
  *     size, S shared experts, G = E + S groups (shared groups last), B = block_m, R = T*K and
@@ -119,7 +120,8 @@ moe_status_t moe_route(const moe_shape_t* shape, const uint16_t* x, const float*
  *   row_token[Mcap]:  token of each row, -1 on padding rows (rows >= total_rows are not written).
  *                     Inside a segment tokens ascend (deterministic, stable).
  *   pos[T,K]:         row of token t's slot j in its expert's segment.
- *   x_perm[Mcap,H]:   x[row_token[r]] or 0 on padding rows, r < total_rows (skipped if x == NULL).
+ *   x_perm[Mcap,H]:   x[row_token[r]] or 0 on padding rows, r < total_rows (skipped if x == NULL;
+ *                     with x given, x and x_perm must be 16-byte aligned).
  * topk_idx entries must lie in [0, E) and be distinct per token (moe_route guarantees it).
  * ws: device scratch of at least moe_workspace_size(shape) bytes (unused when T == 0).
  */

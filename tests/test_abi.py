@@ -191,6 +191,20 @@ def test_gemm_tensors_must_be_16_byte_aligned(lib):
         a[i] = odd
         assert lib.moe_route(ctypes.byref(s), *a, None) == -1
         assert "aligned" in M.moe_last_error()
+    # the row movers: gather (x, x_perm), combine (y_perm, y), combine backward (dy, y_perm,
+    # dy_perm) and the backward unpermute (dx_perm, dx)
+    for i in (1, 7):
+        a = [d] * 8
+        a[i] = odd
+        assert lib.moe_permute(ctypes.byref(s), *a, d, 1 << 20, None) == -1
+        assert "aligned" in M.moe_last_error()
+    for fn, n, idx in (("moe_combine", 5, (0, 4)), ("moe_combine_bwd", 9, (0, 1, 7)),
+                       ("moe_unpermute_bwd", 4, (0, 3))):
+        for i in idx:
+            a = [d] * n
+            a[i] = odd
+            assert _call(lib, fn, ctypes.byref(s), *a, None) == -1, (fn, i)
+            assert "aligned" in M.moe_last_error()
 
 
 def test_workspace_too_small(lib):

@@ -306,6 +306,9 @@ def test_empty_batch():
     M.grouped_gemm_bwd(s, M.MOE_WGRAD, buf["x_perm"], buf["h_save"], buf["a"], buf["dy_perm"],
                        buf["seg_offsets"], None, None, None, None, buf["dh"], None, buf["dw1"],
                        buf["dw2"])
+    counts = torch.full((8,), 7, dtype=torch.int32, device=DEV)
+    M.moe_route(s, None, None, None, None, None, None, None, None, counts)
     torch.cuda.synchronize()
     assert np.all(_np(buf["seg_offsets"]) == 0) and int(_np(buf["total_rows"])[0]) == 0
     assert float(buf["dw1"].float().abs().sum()) == 0 and float(buf["dw2"].float().abs().sum()) == 0
+    assert np.all(_np(counts) == 0)   # no token routed: every count is zero
