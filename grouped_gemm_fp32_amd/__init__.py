@@ -129,6 +129,28 @@ def _ptr(t, name, dtype=None):
     return t.data_ptr()
 
 
+def _need(shape, **sizes):
+    """Raise if a tensor argument holds fewer elements than its layout needs for this shape.
+
+    The C entry points take bare pointers and cannot see sizes, so a short tensor would let a
+    kernel read or write past it; this is checked here instead. Sizes are given as element counts
+    per argument name; tensors passed as None or as raw integer addresses are not checked. An
+    invalid shape is left to the C call to report."""
+    if moe_row_capacity(shape) < 0:
+        return
+    for name, (t, n) in sizes.items():
+        if t is None or isinstance(t, int):
+            continue
+        if t.numel() < n:
+            raise ValueError(f"{name} has {t.numel()} elements; {shape!r} needs at least {n}")
+
+
+def _dims(shape):
+    """T, H, E, K, I, G and the row capacity of the permuted buffers."""
+    return (shape.T, shape.H, shape.E, shape.K, shape.I, shape.E + shape.S,
+            max(0, moe_row_capacity(shape)))
+
+
 def _stream(stream, *tensors):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -184,6 +206,10 @@ def moe_workspace_size(shape: MoeShape) -> int:
 def moe_route(shape, x, w_gate, logit_bias, sel_bias, logits, probs, topk_idx, topk_w,
               expert_counts, stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, x=(x, T * H), w_gate=(w_gate, E * H), logit_bias=(logit_bias, E),
+          sel_bias=(sel_bias, E), logits=(logits, T * E), probs=(probs, T * E),
+          topk_idx=(topk_idx, T * K), topk_w=(topk_w, T * K), expert_counts=(expert_counts, E))
     st = _stream(stream, topk_idx, expert_counts)
     _check("moe_route", lib.moe_route(
         ctypes.byref(shape), _ptr(x, "x", _bf16()), _ptr(w_gate, "w_gate", _f32()),
@@ -196,6 +222,10 @@ def moe_route(shape, x, w_gate, logit_bias, sel_bias, logits, probs, topk_idx, t
 def moe_permute(shape, topk_idx, x, seg_offsets, tile_group, total_rows, row_token, pos, x_perm,
                 ws, stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, topk_idx=(topk_idx, T * K), x=(x, T * H), seg_offsets=(seg_offsets, G + 1),
+          tile_group=(tile_group, mcap // shape.block_m), total_rows=(total_rows, 1),
+          row_token=(row_token, mcap), pos=(pos, T * K), x_perm=(x_perm, mcap * H))
     st = _stream(stream, topk_idx)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("moe_permute", lib.moe_permute(
@@ -208,6 +238,11 @@ def moe_permute(shape, topk_idx, x, seg_offsets, tile_group, total_rows, row_tok
 def grouped_gemm_fwd(shape, which, x_perm, seg_offsets, tile_group, total_rows, w1, w2, h_save, a,
                      y_perm, stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, x_perm=(x_perm, mcap * H), seg_offsets=(seg_offsets, G + 1),
+          tile_group=(tile_group, mcap // shape.block_m), total_rows=(total_rows, 1),
+          w1=(w1, G * 2 * I * H), w2=(w2, G * H * I), h_save=(h_save, mcap * 2 * I),
+          a=(a, mcap * I), y_perm=(y_perm, mcap * H))
     st = _stream(stream, a)
     _check("grouped_gemm_fwd", lib.grouped_gemm_fwd(
         ctypes.byref(shape), which, _ptr(x_perm, "x_perm", _bf16()),
@@ -220,6 +255,17 @@ def grouped_gemm_fwd(shape, which, x_perm, seg_offsets, tile_group, total_rows, 
 def grouped_gemm_bwd(shape, which, x_perm, h_save, a, dy_perm, seg_offsets, tile_group, total_rows,
                      w1, w2, dh, dx_perm, dw1, dw2, stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    # The weight gradients follow a caller-supplied segment table, so their row operands are only
+    # checked (against the capacity) when a data-gradient bit is also set.
+    sizes = dict(w1=(w1, G * 2 * I * H), w2=(w2, G * H * I), dw1=(dw1, G * 2 * I * H),
+                 dw2=(dw2, G * H * I), seg_offsets=(seg_offsets, G + 1))
+    if int(which) & MOE_DGRAD:
+        sizes.update(x_perm=(x_perm, mcap * H), h_save=(h_save, mcap * 2 * I), a=(a, mcap * I),
+                     dy_perm=(dy_perm, mcap * H), tile_group=(tile_group, mcap // shape.block_m),
+                     total_rows=(total_rows, 1), dh=(dh, mcap * 2 * I),
+                     dx_perm=(dx_perm, mcap * H))
+    _need(shape, **sizes)
     st = _stream(stream, dw1, dh)
     _check("grouped_gemm_bwd", lib.grouped_gemm_bwd(
         ctypes.byref(shape), which, _ptr(x_perm, "x_perm", _bf16()), _ptr(h_save, "h_save", _bf16()),
@@ -232,6 +278,9 @@ def grouped_gemm_bwd(shape, which, x_perm, h_save, a, dy_perm, seg_offsets, tile
 
 def moe_combine(shape, y_perm, pos, topk_w, seg_offsets, y, stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, y_perm=(y_perm, mcap * H), pos=(pos, T * K), topk_w=(topk_w, T * K),
+          seg_offsets=(seg_offsets, G + 1), y=(y, T * H))
     st = _stream(stream, y_perm)
     _check("moe_combine", lib.moe_combine(
         ctypes.byref(shape), _ptr(y_perm, "y_perm", _bf16()), _ptr(pos, "pos", _i32()),
@@ -242,6 +291,10 @@ def moe_combine(shape, y_perm, pos, topk_w, seg_offsets, y, stream=None):
 def moe_combine_bwd(shape, dy, y_perm, pos, topk_w, seg_offsets, row_token, total_rows, dy_perm,
                     dtopk_w, stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, dy=(dy, T * H), y_perm=(y_perm, mcap * H), pos=(pos, T * K),
+          topk_w=(topk_w, T * K), seg_offsets=(seg_offsets, G + 1), row_token=(row_token, mcap),
+          total_rows=(total_rows, 1), dy_perm=(dy_perm, mcap * H), dtopk_w=(dtopk_w, T * K))
     st = _stream(stream, dy)
     _check("moe_combine_bwd", lib.moe_combine_bwd(
         ctypes.byref(shape), _ptr(dy, "dy", _bf16()), _ptr(y_perm, "y_perm", _bf16()),
@@ -253,6 +306,9 @@ def moe_combine_bwd(shape, dy, y_perm, pos, topk_w, seg_offsets, row_token, tota
 
 def moe_unpermute_bwd(shape, dx_perm, pos, seg_offsets, dx, stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, dx_perm=(dx_perm, mcap * H), pos=(pos, T * K), seg_offsets=(seg_offsets, G + 1),
+          dx=(dx, T * H))
     st = _stream(stream, dx_perm)
     _check("moe_unpermute_bwd", lib.moe_unpermute_bwd(
         ctypes.byref(shape), _ptr(dx_perm, "dx_perm", _bf16()), _ptr(pos, "pos", _i32()),
@@ -262,6 +318,8 @@ def moe_unpermute_bwd(shape, dx_perm, pos, seg_offsets, dx, stream=None):
 def grouped_gemm_wgrad_f32(shape, which, x_perm, a, dy_perm, dh, seg_offsets, dw1, dw2,
                            stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, seg_offsets=(seg_offsets, G + 1), dw1=(dw1, G * 2 * I * H), dw2=(dw2, G * H * I))
     st = _stream(stream, dw1, dw2)
     _check("grouped_gemm_wgrad_f32", lib.grouped_gemm_wgrad_f32(
         ctypes.byref(shape), int(which), _ptr(x_perm, "x_perm", _bf16()), _ptr(a, "a", _bf16()),
@@ -273,6 +331,10 @@ def grouped_gemm_wgrad_f32(shape, which, x_perm, a, dy_perm, dh, seg_offsets, dw
 def moe_route_bwd(shape, dtopk_w, topk_idx, probs, x, w_gate, dlogits, dw_gate, dx_router,
                   stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, dtopk_w=(dtopk_w, T * K), topk_idx=(topk_idx, T * K), probs=(probs, T * E),
+          x=(x, T * H), w_gate=(w_gate, E * H), dlogits=(dlogits, T * E), dw_gate=(dw_gate, E * H),
+          dx_router=(dx_router, T * H))
     st = _stream(stream, dlogits, dw_gate)
     _check("moe_route_bwd", lib.moe_route_bwd(
         ctypes.byref(shape), _ptr(dtopk_w, "dtopk_w", _f32()), _ptr(topk_idx, "topk_idx", _i32()),
@@ -283,6 +345,9 @@ def moe_route_bwd(shape, dtopk_w, topk_idx, probs, x, w_gate, dlogits, dw_gate, 
 
 def moe_router_grads(shape, dlogits, x, w_gate, dw_gate, dx_router, stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, dlogits=(dlogits, T * E), x=(x, T * H), w_gate=(w_gate, E * H),
+          dw_gate=(dw_gate, E * H), dx_router=(dx_router, T * H))
     st = _stream(stream, dlogits, dw_gate, dx_router)
     _check("moe_router_grads", lib.moe_router_grads(
         ctypes.byref(shape), _ptr(dlogits, "dlogits", _f32()), _ptr(x, "x", _bf16()),
@@ -296,6 +361,10 @@ def moe_balance_workspace_size(shape, seq_len) -> int:
 
 def moe_balance_loss(shape, seq_len, alpha, probs, topk_idx, seq_loss, dlogits, ws, stream=None):
     lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    n_seq = T // int(seq_len) if int(seq_len) > 0 else 0
+    _need(shape, probs=(probs, T * E), topk_idx=(topk_idx, T * K), seq_loss=(seq_loss, n_seq),
+          dlogits=(dlogits, T * E))
     st = _stream(stream, probs, seq_loss, dlogits)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("moe_balance_loss", lib.moe_balance_loss(
@@ -306,6 +375,7 @@ def moe_balance_loss(shape, seq_len, alpha, probs, topk_idx, seq_loss, dlogits, 
 
 def moe_bias_update(shape, expert_counts, gamma, sel_bias, stream=None):
     lib = load_library()
+    _need(shape, expert_counts=(expert_counts, shape.E), sel_bias=(sel_bias, shape.E))
     st = _stream(stream, sel_bias)
     _check("moe_bias_update", lib.moe_bias_update(
         ctypes.byref(shape), _ptr(expert_counts, "expert_counts", _i32()), float(gamma),

@@ -232,3 +232,31 @@ def test_binding_refuses_host_tensors(lib):
     with pytest.raises(ValueError):
         M.moe_route(s, None, None, None, None, torch.zeros(4, 8), None, t, torch.zeros(4, 2), None,
                     stream=0)
+
+
+def test_binding_checks_tensor_sizes_against_the_shape(lib):
+    """A tensor shorter than its layout needs is refused before any pointer reaches the library
+    (the C entry points see bare pointers and could not tell)."""
+    import torch
+    s = M.make_shape(64, 256, 8, 2, 128, 1, 16)
+    mcap = M.moe_row_capacity(s)
+    T, H, E, K, I, G = 64, 256, 8, 2, 128, 9
+    with pytest.raises(ValueError, match="topk_idx has 126 elements"):
+        M.moe_route(s, None, None, None, None, torch.zeros(T, E), None,
+                    torch.zeros(T * K - 2, dtype=torch.int32), torch.zeros(T, K), None, stream=0)
+    with pytest.raises(ValueError, match="x_perm"):
+        M.grouped_gemm_fwd(s, M.MOE_FWD, torch.zeros(mcap - 1, H), None, None, None, None, None,
+                           None, None, None, stream=0)
+    with pytest.raises(ValueError, match="w2"):
+        M.grouped_gemm_fwd(s, M.MOE_FWD, None, None, None, None, None,
+                           torch.zeros(G - 1, H, I), None, None, None, stream=0)
+    with pytest.raises(ValueError, match="dw1"):
+        M.grouped_gemm_wgrad_f32(s, M.MOE_WGRAD, None, None, None, None, None,
+                                 torch.zeros(G, 2 * I, H - 1), None, stream=0)
+    with pytest.raises(ValueError, match="seq_loss"):
+        M.moe_balance_loss(s, 16, 0.1, None, None, torch.zeros(3), None, None, stream=0)
+    with pytest.raises(ValueError, match="sel_bias"):
+        M.moe_bias_update(s, None, 0.1, torch.zeros(E - 1), stream=0)
+    # full-size host tensors pass the size check and are then refused as host memory
+    with pytest.raises(ValueError, match="device tensor"):
+        M.moe_bias_update(s, torch.zeros(E, dtype=torch.int32), 0.1, torch.zeros(E), stream=0)

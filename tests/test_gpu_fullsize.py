@@ -286,8 +286,9 @@ def test_decode_256_tokens_full_layer(name):
     if name == "c5e":
         for e in cfg.forced_empty:
             assert seg[e + 1] == seg[e]
-    assert_bf16_close(vals_host(buf["a"])[:total], ref["a"], "a")
-    assert_bf16_close(vals_host(buf["y_perm"])[:total], ref["y_perm"], "y_perm")
+    # rows past total_rows are never written: only the written rows are decoded
+    assert_bf16_close(vals_host(buf["a"][:total]), ref["a"], "a")
+    assert_bf16_close(vals_host(buf["y_perm"][:total]), ref["y_perm"], "y_perm")
     assert_bf16_close(vals_host(buf["y"]), ref["y"], "y")
 
 
