@@ -184,6 +184,9 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, copy a cold buffer of this many MiB (a plain copy of known "
                          "size that scales the HBM byte counters)")
+    ap.add_argument("--materialize", action="store_true",
+                    help="c3/c5: write x_perm in moe_permute and run grouped_gemm_fwd on it instead "
+                         "of gathering x's rows inside the gate/up product")
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens of the workload the CPU oracle runs (0 = skip the CPU baseline); "
                          "default 384 for c2, 256 for c3, all 256 for c5")
@@ -225,6 +228,11 @@ def main():
         route_args = (X, WG, LB, SB, b["logits"])
     torch.cuda.synchronize()
 
+    # Forward-only workloads gather x's rows inside the gate/up product (no x_perm); the training
+    # step keeps x_perm, which the gate/up weight gradient reads.
+    gather = not fwd_bwd and not args.materialize
+    if gather:
+        del b["x_perm"]
     stages = ["route", "permute", "fwd_gateup", "fwd_down", "combine"]
     if fwd_bwd:
         stages += ["combine_bwd", "dgrad_down", "dgrad_gateup", "wgrad_down", "wgrad_gateup",
@@ -238,13 +246,22 @@ def main():
         mark(0)
         M.moe_route(s, *route_args, b["probs"], b["topk_idx"], b["topk_w"], b["expert_counts"])
         mark(1)
-        M.moe_permute(s, b["topk_idx"], X, b["seg_offsets"], b["tile_group"], b["total_rows"],
-                      b["row_token"], b["pos"], b["x_perm"], b["ws"])
-        mark(2)
-        M.grouped_gemm_fwd(s, M.MOE_FWD_GATEUP, b["x_perm"], b["seg_offsets"], b["tile_group"],
-                           b["total_rows"], W1, W2, h_save, b["a"], b["y_perm"])
+        if gather:   # maps only: the gate/up product reads x through row_token
+            M.moe_permute(s, b["topk_idx"], None, b["seg_offsets"], b["tile_group"],
+                          b["total_rows"], b["row_token"], b["pos"], None, b["ws"])
+            mark(2)
+            M.grouped_gemm_fwd_gather(s, M.MOE_FWD_GATEUP, X, b["row_token"], b["seg_offsets"],
+                                      b["tile_group"], b["total_rows"], W1, W2, h_save, b["a"],
+                                      b["y_perm"])
+        else:
+            M.moe_permute(s, b["topk_idx"], X, b["seg_offsets"], b["tile_group"],
+                          b["total_rows"], b["row_token"], b["pos"], b["x_perm"], b["ws"])
+            mark(2)
+            M.grouped_gemm_fwd(s, M.MOE_FWD_GATEUP, b["x_perm"], b["seg_offsets"],
+                               b["tile_group"], b["total_rows"], W1, W2, h_save, b["a"],
+                               b["y_perm"])
         mark(3)
-        M.grouped_gemm_fwd(s, M.MOE_FWD_DOWN, b["x_perm"], b["seg_offsets"], b["tile_group"],
+        M.grouped_gemm_fwd(s, M.MOE_FWD_DOWN, None, b["seg_offsets"], b["tile_group"],
                            b["total_rows"], W1, W2, h_save, b["a"], b["y_perm"])
         mark(4)
         M.moe_combine(s, b["y_perm"], b["pos"], b["topk_w"], b["seg_offsets"], b["y"])
@@ -338,6 +355,8 @@ def main():
         "stages_tflops": {k: round(per_row[k] * rows / (stage_ms[k] * 1e-3) / 1e12, 1)
                           for k in per_row},
         "experts_touched": touched,
+        "permutation": ("rows of x gathered inside the gate/up GEMM (moe_permute writes the maps "
+                        "only, no x_perm)") if gather else "x_perm written by moe_permute",
     }
     # The forward, data-gradient and weight-gradient passes, each its two grouped GEMMs.
     passes = {"fwd": ("fwd_gateup", "fwd_down"), "dx": ("dgrad_down", "dgrad_gateup"),

@@ -16,7 +16,8 @@ __all__ = [
     "MOE_DGRAD_DOWN", "MOE_DGRAD_GATEUP", "MOE_WGRAD_DOWN", "MOE_WGRAD_GATEUP", "MOE_DGRAD",
     "MOE_WGRAD",
     "moe_abi_version", "moe_status_string", "moe_last_error", "moe_row_capacity",
-    "moe_workspace_size", "moe_route", "moe_permute", "grouped_gemm_fwd", "grouped_gemm_bwd",
+    "moe_workspace_size", "moe_route", "moe_permute", "grouped_gemm_fwd",
+    "grouped_gemm_fwd_gather", "grouped_gemm_bwd",
     "grouped_gemm_wgrad_f32", "moe_combine", "moe_combine_bwd", "moe_unpermute_bwd",
     "moe_route_bwd", "moe_router_grads", "moe_balance_loss",
     "moe_balance_workspace_size", "moe_bias_update",
@@ -75,6 +76,7 @@ _SIGS = {
     "moe_route": (ctypes.c_int, [_SP] + [_P] * 10),
     "moe_permute": (ctypes.c_int, [_SP] + [_P] * 9 + [ctypes.c_size_t, _P]),
     "grouped_gemm_fwd": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 10),
+    "grouped_gemm_fwd_gather": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 11),
     "grouped_gemm_bwd": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 14),
     "moe_combine": (ctypes.c_int, [_SP] + [_P] * 6),
     "moe_combine_bwd": (ctypes.c_int, [_SP] + [_P] * 10),
@@ -246,6 +248,23 @@ def grouped_gemm_fwd(shape, which, x_perm, seg_offsets, tile_group, total_rows, 
     st = _stream(stream, a)
     _check("grouped_gemm_fwd", lib.grouped_gemm_fwd(
         ctypes.byref(shape), which, _ptr(x_perm, "x_perm", _bf16()),
+        _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(tile_group, "tile_group", _i32()),
+        _ptr(total_rows, "total_rows", _i32()), _ptr(w1, "w1", _bf16()), _ptr(w2, "w2", _bf16()),
+        _ptr(h_save, "h_save", _bf16()), _ptr(a, "a", _bf16()), _ptr(y_perm, "y_perm", _bf16()),
+        st))
+
+
+def grouped_gemm_fwd_gather(shape, which, x, row_token, seg_offsets, tile_group, total_rows, w1,
+                            w2, h_save, a, y_perm, stream=None):
+    lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, x=(x, T * H), row_token=(row_token, mcap), seg_offsets=(seg_offsets, G + 1),
+          tile_group=(tile_group, mcap // shape.block_m), total_rows=(total_rows, 1),
+          w1=(w1, G * 2 * I * H), w2=(w2, G * H * I), h_save=(h_save, mcap * 2 * I),
+          a=(a, mcap * I), y_perm=(y_perm, mcap * H))
+    st = _stream(stream, a)
+    _check("grouped_gemm_fwd_gather", lib.grouped_gemm_fwd_gather(
+        ctypes.byref(shape), which, _ptr(x, "x", _bf16()), _ptr(row_token, "row_token", _i32()),
         _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(tile_group, "tile_group", _i32()),
         _ptr(total_rows, "total_rows", _i32()), _ptr(w1, "w1", _bf16()), _ptr(w2, "w2", _bf16()),
         _ptr(h_save, "h_save", _bf16()), _ptr(a, "a", _bf16()), _ptr(y_perm, "y_perm", _bf16()),

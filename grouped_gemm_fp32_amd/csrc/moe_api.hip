@@ -195,9 +195,47 @@ moe_status_t grouped_gemm_fwd(const moe_shape_t* s, uint32_t which, const uint16
     REQUIRE_T(w2);
     REQUIRE_T(y_perm);
   }
-  return hip_status(moe::launch_ggemm_fwd(*s, which, capacity(s), x_perm, seg_offsets, tile_group, total_rows,
-                                          w1, w2, h_save, a, y_perm, (hipStream_t)stream),
+  return hip_status(moe::launch_ggemm_fwd(*s, which, capacity(s), x_perm, nullptr, seg_offsets,
+                                          tile_group, total_rows, w1, w2, h_save, a, y_perm,
+                                          (hipStream_t)stream),
                     "grouped_gemm_fwd");
+}
+
+moe_status_t grouped_gemm_fwd_gather(const moe_shape_t* s, uint32_t which, const uint16_t* x,
+                                     const int32_t* row_token, const int32_t* seg_offsets,
+                                     const int32_t* tile_group, const int32_t* total_rows,
+                                     const uint16_t* w1, const uint16_t* w2, uint16_t* h_save,
+                                     uint16_t* a, uint16_t* y_perm, void* stream) {
+  CHECK_SHAPE(s);
+  if (which == 0 || (which & ~(uint32_t)MOE_FWD)) {
+    set_err("which must be a non-empty combination of MOE_FWD_GATEUP and MOE_FWD_DOWN");
+    return MOE_ERR_INVALID_ARG;
+  }
+  // the gathering DMA addresses x with 32-bit byte offsets and a past-the-end marker at 2^31
+  if ((int64_t)s->T * s->H * 2 > (int64_t)1 << 31) {
+    set_err("grouped_gemm_fwd_gather needs T*H*2 <= 2^31 bytes; use moe_permute + grouped_gemm_fwd");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (s->T == 0) return MOE_OK;
+  REQUIRE(seg_offsets);
+  REQUIRE(tile_group);
+  REQUIRE(total_rows);
+  REQUIRE_T(a);
+  if (h_save) REQUIRE_T(h_save);
+  if (which & MOE_FWD_GATEUP) {
+    REQUIRE_T(x);
+    REQUIRE(row_token);
+    REQUIRE_T(w1);
+  }
+  if (which & MOE_FWD_DOWN) {
+    REQUIRE_T(w2);
+    REQUIRE_T(y_perm);
+  }
+  return hip_status(moe::launch_ggemm_fwd(*s, which, capacity(s), x,
+                                          (which & MOE_FWD_GATEUP) ? row_token : nullptr,
+                                          seg_offsets, tile_group, total_rows, w1, w2, h_save, a,
+                                          y_perm, (hipStream_t)stream),
+                    "grouped_gemm_fwd_gather");
 }
 
 moe_status_t grouped_gemm_bwd(const moe_shape_t* s, uint32_t which, const uint16_t* x_perm,

@@ -44,6 +44,10 @@ template <int KIND> struct KindTraits {
 
 struct GemmArgs {
   const uint16_t* a;   // A source
+  // Gathered A rows (forward gate/up only): when set, row r of A is row a_rows[r] of `a` (the
+  // token rows x[T,H], a_bytes bytes in all), and rows with a_rows[r] < 0 (padding) read as zero.
+  const int32_t* a_rows;
+  int64_t a_bytes;
   const uint16_t* b;   // B source
   int64_t lda, ldb;
   int64_t b_gstride;   // elements per group of the B source (weights); 0 for wgrad
@@ -232,9 +236,15 @@ __global__ __launch_bounds__(kThreads, 2) void ggemm_kernel(GemmArgs p) {
   typename LoaderSel<Tr::b_trans, BN>::type lb;
 
   // Row pointers of K-contiguous operands (k offset added by the loader).
-  const uint16_t* a_rows = p.a + (int64_t)m0 * p.lda;
+  const uint16_t* a_tile = p.a + (int64_t)m0 * p.lda;
   const uint16_t* b_grp = p.b + (int64_t)g * p.b_gstride;
-  auto a_row = [&](int r) -> const uint16_t* { return a_rows + (int64_t)r * p.lda; };
+  auto a_row = [&](int r) -> const uint16_t* {
+    if (p.a_rows) {   // gathered rows: padding rows (token < 0) load as zero
+      const int tok = p.a_rows[m0 + r];
+      return tok >= 0 ? p.a + (int64_t)tok * p.lda : nullptr;
+    }
+    return a_tile + (int64_t)r * p.lda;
+  };
   auto b_row = [&](int r) -> const uint16_t* {
     if (Tr::split) {
       const int half = BN / 2;
@@ -422,6 +432,10 @@ __device__ __forceinline__ v4u32_t make_rsrc(const void* base, int64_t bytes) {
   return r;
 }
 
+// A lane offset past the end of every buffer resource the gathering kernels build (their sources
+// hold at most 2^31 bytes, which the host checks): the DMA then deposits zeros.
+constexpr uint32_t kPastEnd = 0x80000000u;
+
 // Bounds-checked DMA of 16 bytes per lane from a buffer resource into LDS at lds_wave + 16 * lane.
 // Issued from asm: the instruction has no register result (it writes LDS through M0), and hiding
 // it from the compiler keeps it from draining every DMA before unrelated LDS reads; the kernel's
@@ -580,7 +594,9 @@ __device__ __forceinline__ void pipe_tile(const GemmArgs& p, unsigned char* smem
 
   // ---- buffer resources: each covers exactly the bytes this tile may read ----------------------
   v4u32_t ra, rb;
+  const bool gather = !AMN && p.a_rows != nullptr;   // A rows gathered from the token rows
   if (AMN) ra = make_rsrc(p.a + (int64_t)kbeg * p.lda, (int64_t)klen * p.lda * 2);
+  else if (gather) ra = make_rsrc(p.a, p.a_bytes);
   else ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)BM * p.lda * 2);
   if (Tr::grouped_rows) rb = make_rsrc(p.b + (int64_t)g * p.b_gstride, p.b_gstride * 2);
   else rb = make_rsrc(p.b + (int64_t)kbeg * p.ldb, (int64_t)klen * p.ldb * 2);
@@ -595,7 +611,12 @@ __device__ __forceinline__ void pipe_tile(const GemmArgs& p, unsigned char* smem
     if constexpr (!AMN) {
       const int r = (i * 4 + wave) * RPI + lane / CPR;
       const int c = kswz<BK>(r, lane % CPR);
-      a_off[i] = (uint32_t)(((int64_t)r * p.lda + c * 8) * 2);
+      if (gather) {
+        const int tok = p.a_rows[m0 + r];
+        a_off[i] = tok >= 0 ? (uint32_t)(((int64_t)tok * p.lda + c * 8) * 2) : kPastEnd;
+      } else {
+        a_off[i] = (uint32_t)(((int64_t)r * p.lda + c * 8) * 2);
+      }
     } else {
       constexpr int CPRM = BM / 8;
       const int f = (i * 4 + wave) * 64 + lane;
@@ -885,9 +906,10 @@ constexpr int kThreads8 = 512;
 // The engine proper: DMA addressing of one tile at a time, fragment reads and the pipelined
 // contraction. A persistent kernel may set up the next tile's DMA while the accumulators of the
 // current one are still live.
-template <int KIND, class TL>
+template <int KIND, class TL, bool GA = false>
 struct Eng8 {
   typedef KindTraits<KIND> Tr;
+  static_assert(!GA || !Tr::a_trans, "gathered rows are a K-major A operand");
   typedef Mfma<32> Mf;
   static constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, WTM = TL::WTM, WTN = TL::WTN;
   static constexpr int TM = TL::TM, TN = TL::TN, NW = TL::NW;
@@ -910,6 +932,7 @@ struct Eng8 {
   struct Dma {
     v4u32_t ra, rb;
     uint32_t a_off0, b_off0;
+    uint32_t a_offs[GA ? TL::LA : 1];   // gathered A: one lane offset per DMA instruction
   };
   uint32_t a_kstep, b_kstep;
 
@@ -928,10 +951,21 @@ struct Eng8 {
   // columns n0.., contraction over [kbeg, kbeg + klen).
   __device__ __forceinline__ void setup(Dma& st, int g, int m0, int n0, int kbeg, int klen) const {
     if (AMN) st.ra = make_rsrc(p.a + (int64_t)kbeg * p.lda, (int64_t)klen * p.lda * 2);
+    else if (GA) st.ra = make_rsrc(p.a, p.a_bytes);
     else st.ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (int64_t)BM * p.lda * 2);
     if (Tr::grouped_rows) st.rb = make_rsrc(p.b + (int64_t)g * p.b_gstride, p.b_gstride * 2);
     else st.rb = make_rsrc(p.b + (int64_t)kbeg * p.ldb, (int64_t)klen * p.ldb * 2);
-    if constexpr (!AMN) {
+    if constexpr (GA) {
+      // instruction i fills tile rows (i*NW + wave)*RPI + lane/CPR; each reads its token's row
+#pragma unroll
+      for (int i = 0; i < TL::LA; ++i) {
+        const int r = (i * NW + wave) * RPI + lane / CPR;
+        const int tok = p.a_rows[m0 + r];
+        st.a_offs[i] = tok >= 0
+            ? (uint32_t)(((int64_t)tok * p.lda + kswz<BK>(r, lane % CPR) * 8) * 2) : kPastEnd;
+      }
+      st.a_off0 = 0;
+    } else if constexpr (!AMN) {
       const int r = wave * RPI + lane / CPR;
       st.a_off0 = (uint32_t)(((int64_t)r * p.lda + kswz<BK>(r, lane % CPR) * 8) * 2);
     } else {
@@ -975,7 +1009,8 @@ struct Eng8 {
             sl + A_BYTES + (d * NW + wave) * 1024);
     } else {
       const int i = d - LB;
-      dma16(st.ra, st.a_off0 + uniform(kt * a_kstep + a_istride(i)), sl + (i * NW + wave) * 1024);
+      if constexpr (GA) dma16(st.ra, st.a_offs[i] + uniform(kt * a_kstep), sl + (i * NW + wave) * 1024);
+      else dma16(st.ra, st.a_off0 + uniform(kt * a_kstep + a_istride(i)), sl + (i * NW + wave) * 1024);
     }
   }
   __device__ __forceinline__ void issue_stage(const Dma& st, int kt, int slot) const {
@@ -1106,10 +1141,10 @@ struct Eng8 {
 };
 
 // One tile on the eight-wavefront engine, epilogue through the freed ring.
-template <int KIND, class TL>
+template <int KIND, class TL, bool GA>
 __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* smem, int g, int m0,
                                            int n0, int kbeg, int klen) {
-  typedef Eng8<KIND, TL> E;
+  typedef Eng8<KIND, TL, GA> E;
   E e(p, smem);
   typename E::Dma st;
   e.setup(st, g, m0, n0, kbeg, klen);
@@ -1142,7 +1177,7 @@ template <int ROWS> struct Tall8 { typedef Tile8<ROWS, kTall8BN, 4, 2> type; };
 
 // Row-grouped kinds with block_m a multiple of 128: every segment is cut into ceil(blocks / 3)
 // tiles of 1 to 3 whole 128-row blocks (the first `extra` tiles one block taller).
-template <int KIND>
+template <int KIND, bool GA>
 __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
   int* pref = reinterpret_cast<int*>(smem);   // tiles before group g (reused by the DMA ring)
@@ -1186,9 +1221,9 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   const int blk0 = local * base + min(local, extra), nblk = base + (local < extra ? 1 : 0);
   const int m0 = p.seg[g] + blk0 * kTallBlk;
   const int n0 = nt * tile_cols<KIND>(kTall8BN);
-  if (nblk == 3) pipe8_tile<KIND, Tall8<384>::type>(p, smem, g, m0, n0, 0, p.K);
-  else if (nblk == 2) pipe8_tile<KIND, Tall8<256>::type>(p, smem, g, m0, n0, 0, p.K);
-  else pipe8_tile<KIND, Tall8<128>::type>(p, smem, g, m0, n0, 0, p.K);
+  if (nblk == 3) pipe8_tile<KIND, Tall8<384>::type, GA>(p, smem, g, m0, n0, 0, p.K);
+  else if (nblk == 2) pipe8_tile<KIND, Tall8<256>::type, GA>(p, smem, g, m0, n0, 0, p.K);
+  else pipe8_tile<KIND, Tall8<128>::type, GA>(p, smem, g, m0, n0, 0, p.K);
 }
 
 // Row-grouped kinds with 64-row tiles (block_m == 64): one block per tile, from tile_group.
@@ -1392,7 +1427,17 @@ hipError_t launch_rows(GemmArgs a, int64_t mcap, hipStream_t st) {
     // sum over groups of ceil(nb_g / 3) <= (sum nb_g + 2 G) / 3, sum nb_g <= mcap / 128
     const int64_t tiles = (mcap / kTallBlk + 2 * (int64_t)a.G) / kTallMaxBlk + 1;
     const int64_t grid = (tiles * a.n_tiles_n + kNumXcd - 1) / kNumXcd * kNumXcd;
-    hipLaunchKernelGGL((ggemm_tall8_kernel<KIND>), dim3((unsigned)grid), dim3(kThreads8), 0, st, a);
+    if constexpr (KIND == kFwdGateUp) {
+      if (a.a_rows) {
+        hipLaunchKernelGGL((ggemm_tall8_kernel<KIND, true>), dim3((unsigned)grid), dim3(kThreads8),
+                           0, st, a);
+        return hipGetLastError();
+      }
+    } else {
+      if (a.a_rows) return hipErrorInvalidValue;   // only the gate/up product gathers its rows
+    }
+    hipLaunchKernelGGL((ggemm_tall8_kernel<KIND, false>), dim3((unsigned)grid), dim3(kThreads8), 0,
+                       st, a);
     return hipGetLastError();
   }
   if (a.tile_group == nullptr || a.total_rows == nullptr) return hipErrorInvalidValue;
@@ -1415,10 +1460,10 @@ hipError_t launch_rows(GemmArgs a, int64_t mcap, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
-                            const uint16_t* x_perm, const int32_t* seg_offsets,
-                            const int32_t* tile_group, const int32_t* total_rows,
-                            const uint16_t* w1, const uint16_t* w2, uint16_t* h_save, uint16_t* a,
-                            uint16_t* y_perm, hipStream_t st) {
+                            const uint16_t* x_perm, const int32_t* row_token,
+                            const int32_t* seg_offsets, const int32_t* tile_group,
+                            const int32_t* total_rows, const uint16_t* w1, const uint16_t* w2,
+                            uint16_t* h_save, uint16_t* a, uint16_t* y_perm, hipStream_t st) {
   GemmArgs g{};
   g.block_m = s.block_m;
   g.I = s.I;
@@ -1427,7 +1472,10 @@ hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
   g.tile_group = tile_group;
   g.total_rows = total_rows;
   // gate/up + SwiGLU: N counts gate columns (I); each tile covers BN/2 gate + BN/2 up columns.
+  // With row_token the A operand is x[T,H] itself, each row read through the permutation map.
   g.a = x_perm; g.lda = s.H;
+  g.a_rows = row_token;
+  g.a_bytes = row_token ? (int64_t)s.T * s.H * 2 : 0;
   g.b = w1; g.ldb = s.H; g.b_gstride = (int64_t)2 * s.I * s.H;
   g.out = a; g.ldo = s.I; g.out2 = h_save;
   g.N = s.I; g.K = s.H;
@@ -1438,6 +1486,7 @@ hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
   if (!(which & MOE_FWD_DOWN)) return hipSuccess;
   // down
   g.a = a; g.lda = s.I;
+  g.a_rows = nullptr; g.a_bytes = 0;
   g.b = w2; g.ldb = s.I; g.b_gstride = (int64_t)s.H * s.I;
   g.out = y_perm; g.ldo = s.H; g.out2 = nullptr;
   g.N = s.H; g.K = s.I;

@@ -24,9 +24,11 @@ hipError_t launch_permute(const moe_shape_t& s, int64_t mcap, const int32_t* top
                           int32_t* total_rows, int32_t* row_token, int32_t* pos, uint16_t* x_perm,
                           int32_t* ws, hipStream_t st);
 
+// x_perm: the permuted rows [Mcap,H], or (row_token != NULL) the token rows x[T,H], which the
+// gate/up product then reads through row_token (T*H*2 must not exceed 2^31 bytes).
 hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap, const uint16_t* x_perm,
-                            const int32_t* seg_offsets, const int32_t* tile_group,
-                            const int32_t* total_rows,
+                            const int32_t* row_token, const int32_t* seg_offsets,
+                            const int32_t* tile_group, const int32_t* total_rows,
                             const uint16_t* w1, const uint16_t* w2, uint16_t* h_save, uint16_t* a,
                             uint16_t* y_perm, hipStream_t st);
 

@@ -147,6 +147,25 @@ moe_status_t grouped_gemm_fwd(const moe_shape_t* shape, uint32_t which, const ui
                               uint16_t* h_save, uint16_t* a, uint16_t* y_perm, void* stream);
 
 /*
+ * grouped_gemm_fwd_gather — grouped_gemm_fwd with the permutation's row copy left out (TR section
+ * 3.2: the segments stay block-aligned; only where the rows come from changes). The gate/up
+ * product reads row r of its A operand straight from the token rows: x[row_token[r]] for
+ * row_token[r] >= 0 and zero on padding rows (row_token[r] == -1), so moe_permute can be called
+ * with x == NULL and no x_perm buffer exists. row_token [Mcap] and the segments come from that
+ * moe_permute call. Every output equals grouped_gemm_fwd's on the x_perm moe_permute would have
+ * written, bit for bit (same operands, same arithmetic).
+ * For inference: the weight gradient of the gate/up projection (grouped_gemm_bwd) still reads an
+ * x_perm. x [T,H] bf16, 16-byte aligned; needs T*H*2 <= 2^31 bytes (else MOE_ERR_UNSUPPORTED).
+ * Other arguments, layouts and errors as grouped_gemm_fwd; x and row_token are unused (may be
+ * NULL) for MOE_FWD_DOWN alone.
+ */
+moe_status_t grouped_gemm_fwd_gather(const moe_shape_t* shape, uint32_t which, const uint16_t* x,
+                                     const int32_t* row_token, const int32_t* seg_offsets,
+                                     const int32_t* tile_group, const int32_t* total_rows,
+                                     const uint16_t* w1, const uint16_t* w2, uint16_t* h_save,
+                                     uint16_t* a, uint16_t* y_perm, void* stream);
+
+/*
  * grouped_gemm_bwd — gradients of the grouped expert FFN with the routing held fixed.
  *   MOE_DGRAD_DOWN (dy_perm, h_save, w2 -> dh):
  *     da = dy_perm[r] . w2[g]  (fp32);  g_ = h_save gate, u_ = h_save up, s = sigmoid(g_)

@@ -260,3 +260,35 @@ def test_binding_checks_tensor_sizes_against_the_shape(lib):
     # full-size host tensors pass the size check and are then refused as host memory
     with pytest.raises(ValueError, match="device tensor"):
         M.moe_bias_update(s, torch.zeros(E, dtype=torch.int32), 0.1, torch.zeros(E), stream=0)
+
+
+def test_gather_forward_checks(lib):
+    """grouped_gemm_fwd_gather: x and row_token replace x_perm for the gate/up product."""
+    s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
+    d, odd = ctypes.c_void_p(16), ctypes.c_void_p(24)
+    full = [d] * 10   # x, row_token, seg_offsets, tile_group, total_rows, w1, w2, h_save, a, y_perm
+    assert lib.grouped_gemm_fwd_gather(ctypes.byref(s), 0, *full, None) == -1
+    assert lib.grouped_gemm_fwd_gather(ctypes.byref(s), 4, *full, None) == -1
+    for i in range(10):
+        if i == 7:        # h_save is optional
+            continue
+        a = list(full)
+        a[i] = None
+        assert lib.grouped_gemm_fwd_gather(ctypes.byref(s), M.MOE_FWD, *a, None) == -1, i
+        assert "NULL" in M.moe_last_error()
+    for i in (0, 5, 6, 7, 8, 9):   # bf16 tensors: x, w1, w2, h_save, a, y_perm
+        a = list(full)
+        a[i] = odd
+        assert lib.grouped_gemm_fwd_gather(ctypes.byref(s), M.MOE_FWD, *a, None) == -1, i
+        assert "aligned" in M.moe_last_error()
+    # the down product alone reads neither x nor row_token
+    a = list(full)
+    a[0] = a[1] = None
+    st = M.make_shape(0, 256, 8, 2, 128, 1, 16)
+    assert lib.grouped_gemm_fwd_gather(ctypes.byref(st), M.MOE_FWD_DOWN, *a, None) == 0
+    # x addressed with 32-bit byte offsets: T*H*2 <= 2^31
+    big = M.make_shape(262144, 8192, 8, 2, 128, 1, 128)
+    assert lib.grouped_gemm_fwd_gather(ctypes.byref(big), M.MOE_FWD, *full, None) == -2
+    assert "2^31" in M.moe_last_error()
+    empty = M.make_shape(0, 256, 8, 2, 128, 1, 16)
+    assert lib.grouped_gemm_fwd_gather(ctypes.byref(empty), M.MOE_FWD, *([None] * 10), None) == 0
