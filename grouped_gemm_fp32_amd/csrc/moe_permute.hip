@@ -77,15 +77,27 @@ __global__ __launch_bounds__(kSegThreads) void perm_segment_kernel(
     cnt[e] = run;
   }
   __syncthreads();
-  if (tid == 0) {
-    int off = 0;
-    for (int g = 0; g < G; ++g) {
-      seg[g] = off;
+  // Padded group sizes, exclusive prefix sum by the first wavefront, 64 groups per step (shared
+  // groups last, T rows each).
+  if (tid < 64) {
+    int run = 0;
+    for (int base = 0; base < G; base += 64) {
+      const int g = base + tid;
       const int c = g < E ? cnt[g] : T;
-      off += (c + B - 1) / B * B;
+      const int padded = g < G ? (c + B - 1) / B * B : 0;
+      int x = padded;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (tid >= o) x += y;
+      }
+      if (g < G) seg[g] = run + x - padded;
+      run += __shfl(x, 63, 64);
     }
-    seg[G] = off;
-    total_rows[0] = off;
+    if (tid == 0) {
+      seg[G] = run;
+      total_rows[0] = run;
+    }
   }
   __syncthreads();
   for (int i = tid; i < nblk * E; i += kSegThreads) ws[i] = tab[i];
