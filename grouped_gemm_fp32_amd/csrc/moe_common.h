@@ -30,6 +30,23 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return f2bf(lo) | (f2bf(hi) << 16);
 }
 
+// Exact split of 8 fp32 values into three bf16 vectors with hi + mid + lo == w (each part is the
+// remainder rounded to bf16, so every subtraction is exact in fp32).
+__device__ __forceinline__ void split3(const float4& w0, const float4& w1, bf16x8_t& hi,
+                                       bf16x8_t& mid, bf16x8_t& lo) {
+  float r[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = (__bf16)r[i];
+    hi[i] = h;
+    r[i] -= (float)h;
+    const __bf16 m = (__bf16)r[i];
+    mid[i] = m;
+    r[i] -= (float)m;
+    lo[i] = (__bf16)r[i];
+  }
+}
+
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -40,23 +40,6 @@ __device__ __forceinline__ uint32_t key_code(float k) {
 constexpr int kLgTile = 32;      // experts per workgroup (the MFMA's 32)
 constexpr int kLgLargeT = 4096;  // from this many tokens the logits use two token blocks per wave
 
-// Exact split of 8 fp32 values into three bf16 vectors with hi + mid + lo == w (each part is the
-// remainder rounded to bf16, so every subtraction is exact in fp32).
-__device__ __forceinline__ void split3(const float4& w0, const float4& w1, bf16x8_t& hi,
-                                       bf16x8_t& mid, bf16x8_t& lo) {
-  float r[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const __bf16 h = (__bf16)r[i];
-    hi[i] = h;
-    r[i] -= (float)h;
-    const __bf16 m = (__bf16)r[i];
-    mid[i] = m;
-    r[i] -= (float)m;
-    lo[i] = (__bf16)r[i];
-  }
-}
-
 // logits[t0.., e0..] for TB x 32 tokens and 32 experts. Lanes 0-31 hold token (B) and expert (A)
 // rows r = lane; within a 64-k step lane half h = lane >> 5 covers k = 32 h + 8 s .. +8 in slice s
 // (the same assignment for both operands, so each MFMA sums matching pairs and four slices cover

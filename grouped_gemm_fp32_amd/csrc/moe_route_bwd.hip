@@ -12,12 +12,14 @@
 //                       does), c = sum_k w_k dw_k, dlogits = w_k (dw_k - c) on the selected experts
 //                       and 0 elsewhere; unnormalised weights: c = sum_k p_k dw_k and
 //                       dlogits_e = p_e (g_e - c) with g_e = dw_k on the selected experts.
-//   router_dwg_kernel   dWg[E,H] = dlogits^T x, an fp32 contraction over the tokens on the fp32
-//                       matrix unit (v_mfma_f32_32x32x2_f32): one workgroup per 32 x 64 tile of dWg,
-//                       its eight wavefronts take an eighth of the tokens each and their partial
-//                       sums are added in wavefront order (deterministic).
-//   router_dx_kernel    dx_router[T,H] = dlogits Wg, the same instruction with the contraction
-//                       over the experts: a 64-token tile of dlogits in LDS, Wg read from L2.
+//   router_dwg_kernel   dWg[E,H] = dlogits^T x, a contraction over the tokens on the bf16 matrix
+//                       unit with dlogits split exactly into three bf16 parts (exact products,
+//                       fp32 sums): one workgroup per 32 x 64 tile of dWg, its eight wavefronts
+//                       take an eighth of the tokens each and their partial sums are added in
+//                       wavefront order (deterministic).
+//   router_dx_kernel    dx_router[T,H] = dlogits Wg, an fp32 contraction over the experts on the
+//                       fp32 matrix unit (v_mfma_f32_32x32x2_f32): a 64-token tile of dlogits in
+//                       LDS, Wg read from L2.
 //   balance_hist_kernel, balance_kernel, balance_reduce_kernel
 //                       per-chunk selection counts, then the sequence-wise balance loss (per sequence alpha sum_e f_e P_e, f the
 //                       normalised selection counts, P the mean probabilities) as per-chunk
@@ -83,64 +85,142 @@ __global__ __launch_bounds__(kThreads) void route_bwd_kernel(int T, int E, int K
 }
 
 // ---- dWg = dlogits^T x ----------------------------------------------------------------------------
-// MFMA 32x32x2 f32: lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32]; the result D[i][j]
-// sits in lane j (+32 for rows 4..7 of each group of 8), register q -> row 8 (q / 4) + 4 (l / 32)
-// + q % 4.
-// A workgroup of eight wavefronts covers a 32 x 64 tile of dWg; each wavefront takes an eighth of
-// the tokens for the whole tile, as two MFMA blocks (even and odd columns) that share each dlogits
-// operand, so every lane loads one fp32 and one bf16 pair per two MFMAs. The partial sums are
+// On the bf16 matrix unit: each fp32 dlogits value is split exactly into three bf16 parts
+// (hi + mid + lo, split3), and x is bf16, so every product is exact in fp32. The three parts' sums
+// are kept in separate accumulators and added as (lo + mid) + hi at the end: the fp32 contraction
+// up to summation order, with no more roundings per element than one fp32 sum over the tokens.
+// v_mfma_f32_32x32x16_bf16: lane l supplies A[l % 32][8 (l / 32) .. +7] and B[8 (l / 32) .. +7]
+// [l % 32]; D[i][j] sits in lane j (+32 for rows 4..7 of each group of 8), register q -> row
+// 8 (q / 4) + 4 (l / 32) + q % 4.
+// A workgroup of eight wavefronts covers a 32 x 64 tile of dWg. Wavefront w takes the w-th eighth
+// of the 16-token slices. Per slice each lane loads 16 bytes of dlogits (4 experts of one token)
+// and 16 bytes of x; the dlogits values are split in registers, and the three bf16 parts and x go
+// through the wavefront's own LDS tiles [16 tokens][columns] to come back transposed
+// (ds_read_tr16_b64) as the A operand (32 experts) and the B operands (two 32-column blocks). The
+// next slices' operands load during the current ones' MFMAs. The wavefronts' partial sums are
 // added in wavefront order (deterministic).
 constexpr int kDwgThreads = 512;
-constexpr int kDwgUnroll = 16;  // token pairs per batch; the next batch's operands load during it
+constexpr int kDwgSlices = 4;        // 16-token slices per batch
+// LDS bytes per token row: 64 for a 32-expert bf16 part, 192 for the 64-column x tile (128 used).
+// With row strides of 16 or 48 banks the 16 lanes of a transposed read hit distinct banks.
+constexpr int kDwgARow = 64, kDwgXRow = 192;
+constexpr int kDwgWaveLds = 3 * 16 * kDwgARow + 16 * kDwgXRow;   // 3 KiB of parts + 3 KiB of x
+typedef short dwg_v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dwg_v4i16_t dwg_lds_v4i16_t;
 
+// Operand of the 32 columns col0.. of a [16 tokens][columns] bf16 tile with ROW bytes per token:
+// within 16 lanes, lane i reads 4 columns of token row (i / 4) and the transposing read hands it
+// column col0 + i of 4 consecutive tokens; two reads give 8 (lanes 32-63: tokens 8-15).
+template <int ROW>
+__device__ __forceinline__ bf16x8_t dwg_frag(const unsigned char* tile, int col0, int lane) {
+  const int grp = lane >> 4, li = lane & 15;
+  const int col = col0 + (grp & 1) * 16 + 4 * (li & 3);
+  const int k0 = (grp >> 1) * 8 + (li >> 2);
+  const unsigned char* p0 = tile + k0 * ROW + col * 2;
+  const dwg_v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dwg_lds_v4i16_t*)p0);
+  const dwg_v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dwg_lds_v4i16_t*)(p0 + 4 * ROW));
+  bf16x8_t r;
+  __builtin_memcpy(&r, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi, 8);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t bf_pair(__bf16 a, __bf16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// VEC: dlogits rows are 16-byte aligned (E % 4 == 0 and an aligned base): one float4 per chunk.
+template <bool VEC>
 __global__ __launch_bounds__(kDwgThreads) void router_dwg_kernel(int T, int H, int E,
                                                                  const float* __restrict__ dz,
                                                                  const uint16_t* __restrict__ x,
                                                                  float* __restrict__ dwg) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[8][kDwgWaveLds];
   __shared__ float red[8][32][65];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e0 = blockIdx.x * 32, h0 = blockIdx.y * 64;
   const int r = lane & 31, kh = lane >> 5;
-  const int e = e0 + r;
-  const bool e_ok = e < E;
-  // this wave's eighth of the tokens, in pairs (one k-step of the MFMA each)
-  const int per = (((T + 7) / 8) + 1) & ~1;
-  const int ta = min(T, wave * per), tz = min(T, ta + per);
-  const uint32_t* x2 = reinterpret_cast<const uint32_t*>(x);   // H is even: pairs never straddle rows
-  auto load = [&](int t0, float (&a)[kDwgUnroll], uint32_t (&b)[kDwgUnroll]) {
+  const int nsl = (T + 15) / 16;
+  const int per = (nsl + 7) / 8;
+  const int sa = min(nsl, wave * per), sz = min(nsl, sa + per);   // this wave's slices
+  unsigned char* ap = lds[wave];                    // parts hi, mid, lo: [16][32] bf16 each
+  unsigned char* xt = lds[wave] + 3 * 16 * kDwgARow; // x: [16][64] bf16
+  // A lane's chunks of a slice (two of each): dlogits token row (lane >> 3) (+8), experts
+  // e0 + 4 (lane & 7) .. +3; x token row (lane >> 3) (+8), columns h0 + 8 (lane & 7) .. +7.
+  const int cr = lane >> 3, ce = 4 * (lane & 7), cx = 8 * (lane & 7);
+  struct Ops {
+    float4 a[kDwgSlices][2];
+    uint4 b[kDwgSlices][2];
+  };
+  auto load = [&](int s0, Ops& o) {
 #pragma unroll
-    for (int u = 0; u < kDwgUnroll; ++u) {
-      const int t = t0 + 2 * u + kh;
-      const bool ok = t < tz;
-      a[u] = (ok && e_ok) ? dz[(int64_t)t * E + e] : 0.0f;
-      b[u] = ok ? x2[((int64_t)t * H + h0) / 2 + r] : 0u;
+    for (int j = 0; j < kDwgSlices; ++j) {
+      const int s = s0 + j;
+      const bool live = s < sz;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = s * 16 + cr + 8 * i;
+        const bool tok = live && t < T;
+        const float* row = dz + (int64_t)t * E + e0 + ce;
+        if (VEC) {
+          o.a[j][i] = (tok && e0 + ce < E) ? *reinterpret_cast<const float4*>(row)
+                                            : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        } else {
+          const int n = E - (e0 + ce);   // experts of this chunk inside E
+          o.a[j][i] = make_float4(tok && n > 0 ? row[0] : 0.0f, tok && n > 1 ? row[1] : 0.0f,
+                                  tok && n > 2 ? row[2] : 0.0f, tok && n > 3 ? row[3] : 0.0f);
+        }
+        o.b[j][i] = tok ? *reinterpret_cast<const uint4*>(x + (int64_t)t * H + h0 + cx)
+                        : make_uint4(0, 0, 0, 0);
+      }
     }
   };
-  f32x16_t acc0, acc1;   // columns h0 + 2 r and h0 + 2 r + 1
+  f32x16_t acc[3][2];   // [part: hi, mid, lo][32-column block]
 #pragma unroll
-  for (int q = 0; q < 16; ++q) { acc0[q] = 0.0f; acc1[q] = 0.0f; }
-  float a[kDwgUnroll];
-  uint32_t b[kDwgUnroll];
-  load(ta, a, b);
-  for (int t0 = ta; t0 < tz; t0 += 2 * kDwgUnroll) {
-    float an[kDwgUnroll];
-    uint32_t bn[kDwgUnroll];
-    load(t0 + 2 * kDwgUnroll, an, bn);   // past tz: zeros, no memory access
+  for (int p = 0; p < 3; ++p)
 #pragma unroll
-    for (int u = 0; u < kDwgUnroll; ++u) {
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], __uint_as_float(b[u] << 16), acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], __uint_as_float(b[u] & 0xffff0000u), acc1,
-                                                  0, 0, 0);
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[p][jb][q] = 0.0f;
+  Ops cur;
+  load(sa, cur);
+  for (int s0 = sa; s0 < sz; s0 += kDwgSlices) {
+    Ops nxt;
+    load(s0 + kDwgSlices, nxt);   // past this wave's slices: zeros, no memory access
+#pragma unroll
+    for (int j = 0; j < kDwgSlices; ++j) {
+      // This wavefront's tiles: its LDS operations run in order, so the transposed reads below
+      // see these writes, and the next slice's writes come after these reads.
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float4 v = cur.a[j][i];
+        bf16x8_t hi, mid, lo;   // elements 0..3 used
+        split3(v, make_float4(0.0f, 0.0f, 0.0f, 0.0f), hi, mid, lo);
+        const int off = (cr + 8 * i) * kDwgARow + ce * 2;
+        *reinterpret_cast<uint2*>(ap + off) = make_uint2(bf_pair(hi[0], hi[1]), bf_pair(hi[2], hi[3]));
+        *reinterpret_cast<uint2*>(ap + 16 * kDwgARow + off) =
+            make_uint2(bf_pair(mid[0], mid[1]), bf_pair(mid[2], mid[3]));
+        *reinterpret_cast<uint2*>(ap + 32 * kDwgARow + off) =
+            make_uint2(bf_pair(lo[0], lo[1]), bf_pair(lo[2], lo[3]));
+        *reinterpret_cast<uint4*>(xt + (cr + 8 * i) * kDwgXRow + cx * 2) = cur.b[j][i];
+      }
+      const bf16x8_t b0 = dwg_frag<kDwgXRow>(xt, 0, lane), b1 = dwg_frag<kDwgXRow>(xt, 32, lane);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const bf16x8_t a = dwg_frag<kDwgARow>(ap + p * 16 * kDwgARow, 0, lane);
+        acc[p][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[p][0], 0, 0, 0);
+        acc[p][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[p][1], 0, 0, 0);
+      }
     }
-#pragma unroll
-    for (int u = 0; u < kDwgUnroll; ++u) { a[u] = an[u]; b[u] = bn[u]; }
+    cur = nxt;
   }
-  // D[e][h]: lane -> column r of the block, register q -> e = e0 + 8 (q / 4) + 4 kh + q % 4
+  // D[e][h]: lane -> column r of each 32-column block, register q -> e = e0 + 8 (q / 4) + 4 kh + q % 4
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int el = 8 * (q >> 2) + 4 * kh + (q & 3);
-    red[wave][el][2 * r] = acc0[q];
-    red[wave][el][2 * r + 1] = acc1[q];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+      red[wave][el][32 * jb + r] = (acc[2][jb][q] + acc[1][jb][q]) + acc[0][jb][q];
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < 32 * 64; idx += kDwgThreads) {
@@ -357,8 +437,13 @@ hipError_t launch_router_grads(const moe_shape_t& s, const float* dlogits, const
     return e;
   }
   if (dw_gate) {
-    hipLaunchKernelGGL(router_dwg_kernel, dim3((unsigned)((s.E + 31) / 32), (unsigned)(s.H / 64)),
-                       dim3(kDwgThreads), 0, st, s.T, s.H, s.E, dlogits, x, dw_gate);
+    const dim3 grid((unsigned)((s.E + 31) / 32), (unsigned)(s.H / 64));
+    if (s.E % 4 == 0 && (uintptr_t)dlogits % 16 == 0)
+      hipLaunchKernelGGL(router_dwg_kernel<true>, grid, dim3(kDwgThreads), 0, st, s.T, s.H, s.E,
+                         dlogits, x, dw_gate);
+    else
+      hipLaunchKernelGGL(router_dwg_kernel<false>, grid, dim3(kDwgThreads), 0, st, s.T, s.H, s.E,
+                         dlogits, x, dw_gate);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

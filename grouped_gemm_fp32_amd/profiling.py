@@ -43,7 +43,8 @@ OUTSIDE_STEP = {
     "ggemm_wgrad8_kernel<4,true>": "fp32-dW wgrad down (outside the step)",
     "ggemm_wgrad8_kernel<5,true>": "fp32-dW wgrad gate/up (outside the step)",
     "route_bwd_kernel<true>": "router backward (outside the step)",
-    "router_dwg_kernel": "router backward (outside the step)",
+    "router_dwg_kernel<true>": "router backward (outside the step)",
+    "router_dwg_kernel<false>": "router backward (outside the step)",
     "router_dx_kernel": "router backward (outside the step)",
     "balance_hist_kernel": "balance loss (outside the step)",
     "balance_kernel": "balance loss (outside the step)",

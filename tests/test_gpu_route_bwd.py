@@ -61,6 +61,7 @@ def _check_contraction(got, ref, bound, name):
     (64, 256, 8, 2),          # the tiny layer's routing
     (333, 256, 20, 4),        # ragged tokens, experts not a multiple of 32
     (101, 128, 256, 8),       # the most experts and slots a shape may have
+    (77, 128, 13, 3),         # E % 4 != 0: dlogits rows not 16-byte aligned (scalar loads)
     (8192, 4096, 128, 6),     # the benchmark shape
 ])
 def test_route_bwd_parity(T, H, E, K, normalize):
@@ -163,14 +164,18 @@ def test_balance_loss_parity(T, E, K, seq_len):
     log(f"  loss {got_loss[:4]}, worst err/bound {float((err / bound).max()):.3f}")
 
 
-def test_router_grads_from_given_dlogits():
+@pytest.mark.parametrize("offset", [0, 1])
+def test_router_grads_from_given_dlogits(offset):
+    """offset 1: dlogits starts 4 bytes past a 16-byte boundary (the scalar-load path)."""
     T, H, E, K = 512, 256, 32, 4
     p, idx, dw, x, wg = _inputs(T, H, E, K, seed=11)
     dz = O.route_backward(p, idx, dw) + O.balance_loss(p, idx, 128, 1e-2)[1].astype(np.float32)
     dz = dz.astype(np.float32)
     s = M.make_shape(T, H, E, K, 128, 0, 16)
     dwg_d, dx_d = torch.empty(E, H, device=DEV), torch.empty(T, H, device=DEV)
-    M.moe_router_grads(s, f32_dev(dz), bf16_dev(x), f32_dev(wg), dwg_d, dx_d)
+    dz_d = torch.empty(T * E + offset, device=DEV)
+    dz_d[offset:] = f32_dev(dz).reshape(-1)
+    M.moe_router_grads(s, dz_d[offset:], bf16_dev(x), f32_dev(wg), dwg_d, dx_d)
     torch.cuda.synchronize()
     xv, adz, awg = O.bf16_to_f64(x), np.abs(dz.astype(np.float64)), np.abs(wg.astype(np.float64))
     ref = O.router_weight_grad(dz, x)
