@@ -235,26 +235,31 @@ __global__ __launch_bounds__(kDwgThreads) void router_dwg_kernel(int T, int H, i
 }
 
 // ---- dx_router = dlogits Wg ---------------------------------------------------------------------
-// A workgroup covers 64 tokens x 128 columns; each wavefront 64 tokens x 32 columns (two MFMA
-// blocks sharing every Wg operand), with the Wg loads of the next batch of experts in flight.
+// A workgroup of eight wavefronts covers 64 tokens x 256 columns (one dlogits tile in LDS for all
+// of them); each wavefront 64 tokens x 32 columns (two MFMA blocks sharing every Wg operand), with
+// the Wg loads of the next batch of experts in flight. Wavefronts past the last column only help
+// load the tile.
 constexpr int kDxTok = 64;
+constexpr int kDxThreads = 512;
+constexpr int kDxCols = 32 * (kDxThreads / 64);   // columns per workgroup
 constexpr int kDxUnroll = 16;  // expert pairs per batch
 
-__global__ __launch_bounds__(kThreads) void router_dx_kernel(int T, int H, int E,
+__global__ __launch_bounds__(kDxThreads) void router_dx_kernel(int T, int H, int E,
                                                              const float* __restrict__ dz,
                                                              const float* __restrict__ wg,
                                                              float* __restrict__ dx) {
   extern __shared__ float tile[];   // [kDxTok][E + 1], sized at launch
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * kDxTok, h0 = blockIdx.y * 128 + wave * 32;
+  const int t0 = blockIdx.x * kDxTok, h0 = blockIdx.y * kDxCols + wave * 32;
   const int nt = min(kDxTok, T - t0);
   const int ld = E + 1;
-  // wavefront w fills rows w, w + 4, ...; a row's experts go across the lanes (coalesced)
+  // wavefront w fills rows w, w + 8, ...; a row's experts go across the lanes (coalesced)
 #pragma unroll 4
-  for (int tl = wave; tl < kDxTok; tl += kThreads / 64)
+  for (int tl = wave; tl < kDxTok; tl += kDxThreads / 64)
     for (int e = lane; e < E; e += 64)
       tile[tl * ld + e] = tl < nt ? dz[(int64_t)(t0 + tl) * E + e] : 0.0f;
   __syncthreads();
+  if (h0 >= H) return;   // no barrier follows
   const int r = lane & 31, kh = lane >> 5;
   auto load = [&](int e0, float (&b)[kDxUnroll]) {
 #pragma unroll
@@ -454,8 +459,9 @@ hipError_t launch_router_grads(const moe_shape_t& s, const float* dlogits, const
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(router_dx_kernel, dim3((unsigned)((s.T + kDxTok - 1) / kDxTok), (unsigned)(s.H / 128)),
-                       dim3(kThreads), lds, st, s.T, s.H, s.E, dlogits, wg, dx_router);
+    hipLaunchKernelGGL(router_dx_kernel,
+                       dim3((unsigned)((s.T + kDxTok - 1) / kDxTok), (unsigned)((s.H + kDxCols - 1) / kDxCols)),
+                       dim3(kDxThreads), lds, st, s.T, s.H, s.E, dlogits, wg, dx_router);
     e = hipGetLastError();
   }
   return e;
