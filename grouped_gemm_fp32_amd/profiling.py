@@ -29,8 +29,9 @@ import sys
 
 # rocprofv3 kernel name -> the stage names bench.py reports
 STAGE_OF = {
-    "ggemm_tall8_kernel<0>": "fwd_gateup", "ggemm_tall8_kernel<1>": "fwd_down",
-    "ggemm_tall8_kernel<2>": "dgrad_down", "ggemm_tall8_kernel<3>": "dgrad_gateup",
+    "ggemm_tall8_kernel<0,false>": "fwd_gateup", "ggemm_tall8_kernel<1,false>": "fwd_down",
+    "ggemm_tall8_kernel<2,false>": "dgrad_down", "ggemm_tall8_kernel<3,false>": "dgrad_gateup",
+    "ggemm_tall8_kernel<0,true>": "fwd_gateup",   # rows gathered through row_token
     "ggemm_wgrad8_kernel<4,false>": "wgrad_down", "ggemm_wgrad8_kernel<5,false>": "wgrad_gateup",
     "gather_rows_kernel": "permute", "gather_sum_kernel<true>": "combine",
     "combine_bwd_kernel": "combine_bwd", "gather_sum_kernel<false>": "unpermute_bwd",

@@ -9,7 +9,8 @@ from grouped_gemm_fp32_amd import profiling as P
 COLS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
         "End_Timestamp"]
 GATHER = "void moe::(anonymous namespace)::gather_rows_kernel(int const*, int)"
-TALL0 = "void moe::(anonymous namespace)::ggemm_tall8_kernel<0>(moe::(anonymous namespace)::GemmArgs)"
+TALL0 = ("void moe::(anonymous namespace)::ggemm_tall8_kernel<0, false>"
+         "(moe::(anonymous namespace)::GemmArgs)")
 COPY = "void at::native::vectorized_elementwise_kernel<4, at::native::AddFunctor<int> >(int)"
 FILL = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<int> >(int)"
 
@@ -68,8 +69,8 @@ def test_mfma_utilisation(tmp_path):
                  (disp, TALL0, "GRBM_GUI_ACTIVE", 8 * 2000.0, 100, 100 + ns)]
     rows.append((6, GATHER, "GRBM_GUI_ACTIVE", 80.0, 0, 5))   # no matrix instructions: skipped
     u = P.mfma_util(_write(tmp_path / "m", rows))
-    assert set(u) == {"ggemm_tall8_kernel<0>"}
-    e = u["ggemm_tall8_kernel<0>"]
+    assert set(u) == {"ggemm_tall8_kernel<0,false>"}
+    e = u["ggemm_tall8_kernel<0,false>"]
     assert e["dispatches"] == 2
     assert e["cycles_per_inst"] == pytest.approx(32.0)
     assert e["busy_frac"] == pytest.approx(32000 / (1024 * 2000))
