@@ -52,7 +52,28 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    build_c_example()
     return LIB
+
+
+C_EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi", "moe_c_example.c")
+C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi", "moe_c_example")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_example() -> str:
+    """The plain-C caller of the ABI that the GPU tests run (gcc, the HIP runtime's C API, no
+    Python): linked against libmoe.so through an rpath relative to its own directory."""
+    if not os.path.exists(C_EXAMPLE_SRC):
+        return ""
+    rel = os.path.relpath(PKG, os.path.dirname(C_EXAMPLE))
+    tmp = C_EXAMPLE + ".tmp"
+    _run(["gcc", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"), C_EXAMPLE_SRC,
+          "-o", tmp, "-L", PKG, "-lmoe", f"-Wl,-rpath,$ORIGIN/{rel}",
+          "-L", os.path.join(ROCM, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"])
+    os.replace(tmp, C_EXAMPLE)
+    return C_EXAMPLE
 
 
 if __name__ == "__main__":
