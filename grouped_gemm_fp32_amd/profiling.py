@@ -54,9 +54,25 @@ OUTSIDE_STEP = {
 }
 
 
+# Other kernels of a stage (labels only: STAGE_OF keeps one kernel per stage for the traffic table).
+PART_OF = {
+    "router_logits_kernel<2,4>": "route (router logits)", "router_logits_kernel<1,8>": "route (router logits)",
+    "fill_i32_kernel": "route (count clear)",
+    "perm_hist_kernel": "permute (segments)", "perm_segment_kernel": "permute (segments)",
+    "perm_scatter_kernel": "permute (maps)", "zero_pad_rows_kernel": "combine_bwd (padding rows)",
+    "ggemm_kernel<0,16,256,16,1>": "fwd_gateup (16-row tiles)",
+    "ggemm_kernel<1,16,256,16,1>": "fwd_down (16-row tiles)",
+    "ggemm_kernel<0,32,256,32,1>": "fwd_gateup (32-row tiles)",
+    "ggemm_kernel<1,32,256,32,1>": "fwd_down (32-row tiles)",
+    "ggemm_block64_kernel<0>": "fwd_gateup (64-row tiles)", "ggemm_block64_kernel<1>": "fwd_down (64-row tiles)",
+}
+
+
 def label(k: str) -> str:
     if k in STAGE_OF:
         return STAGE_OF[k]
+    if k in PART_OF:
+        return PART_OF[k]
     if k in OUTSIDE_STEP:
         return OUTSIDE_STEP[k]
     if k.startswith("Cijk_"):
