@@ -193,9 +193,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): this build "
-              f"implements the single-GPU path only; sharding across GPUs is described in DESIGN.md "
-              f"but not implemented.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): the library "
+              f"implements the single-GPU path only; sharding the experts across GPUs (an "
+              f"all-to-all of the permuted rows each way) is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -747,7 +747,6 @@ __device__ __forceinline__ void pipe_tile(const GemmArgs& p, unsigned char* smem
 
 // Row-grouped 64-row tiles (block_m == 64) on the four-wavefront engine.
 typedef Tile<64, 256, 2, 64> Block64Tile;
-typedef Tile<256, 256, 2, 32> WgradTile;
 
 // Columns of output one tile covers (gate/up: gate columns; the tile also covers as many up).
 template <int KIND> constexpr int tile_cols(int bn) { return KindTraits<KIND>::split ? bn / 2 : bn; }
