@@ -183,6 +183,8 @@ template <int ROWS> struct LoaderSel<true, ROWS> { typedef LoaderT<ROWS> type; }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
+constexpr int64_t kSmallRowsBytes = 32ll << 20;   // activation bytes of a "small batch"
+
 template <int KIND, int BM, int BN, int MS, int WAVES_M>
 __global__ __launch_bounds__(kThreads, 2) void ggemm_kernel(GemmArgs p) {
   typedef KindTraits<KIND> Tr;
@@ -203,10 +205,17 @@ __global__ __launch_bounds__(kThreads, 2) void ggemm_kernel(GemmArgs p) {
   int g, m0, n0, kbeg, klen;
   if (Tr::grouped_rows) {
     const int total = p.total_rows[0];
-    const int64_t n_valid = (int64_t)(total / BM) * p.n_tiles_n;
+    const int n_mt = total / BM;
+    const int64_t n_valid = (int64_t)n_mt * p.n_tiles_n;
     const int64_t L = xcd_remap(blockIdx.x, n_valid);
     if (L < 0) return;
-    const int mt = (int)(L / p.n_tiles_n), nt = (int)(L % p.n_tiles_n);
+    // Small batches (the activation rows fit the last-level cache many times over): column-tile
+    // major, so an expert's row blocks are consecutive workgroups that stream the same weight
+    // panel together and share it through L2. Otherwise row-block major, so a row block's column
+    // tiles share its activation panel.
+    const bool nt_major = (int64_t)total * p.lda * 2 <= kSmallRowsBytes;
+    const int mt = nt_major ? (int)(L % n_mt) : (int)(L / p.n_tiles_n);
+    const int nt = nt_major ? (int)(L / n_mt) : (int)(L % p.n_tiles_n);
     m0 = mt * BM;
     n0 = nt * (Tr::split ? BN / 2 : BN);
     g = p.tile_group[m0 / p.block_m];
