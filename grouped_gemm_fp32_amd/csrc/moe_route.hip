@@ -22,7 +22,7 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kRouteWaves = 2048;   // target wavefront count of the routing kernel
+constexpr int kRouteWaves = 8192;   // target wavefront count of the routing kernel
 constexpr int kMaxE = 256;
 
 enum RouteMode { kFromLogits = 1, kFromProbs = 2 };
@@ -319,7 +319,10 @@ hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg
   }
   if (x) {
     const unsigned ge = (unsigned)((s.E + kLgTile - 1) / kLgTile);
-    if (s.T >= kLgLargeT)
+    if (s.T >= 4 * kLgLargeT)
+      hipLaunchKernelGGL((router_logits_kernel<4, 4>), dim3((unsigned)((s.T + 127) / 128), ge), dim3(256),
+                         0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
+    else if (s.T >= kLgLargeT)
       hipLaunchKernelGGL((router_logits_kernel<2, 4>), dim3((unsigned)((s.T + 63) / 64), ge), dim3(256),
                          0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
     else
