@@ -58,6 +58,7 @@ struct GemmArgs {
   uint16_t* out2;      // h_save written by the forward gate/up epilogue (may be null)
   int M, N, K, I;
   int block_m;
+  int max_blk;         // tall tiles: at most this many 128-row blocks per tile (2 or 3)
   int n_tiles_n, n_tiles_m;
   int G;
   const int32_t* tile_group;
@@ -1183,8 +1184,9 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
 constexpr int kTall8BN = 256;
 template <int ROWS> struct Tall8 { typedef Tile8<ROWS, kTall8BN, 4, 2> type; };
 
-// Row-grouped kinds with block_m a multiple of 128: every segment is cut into ceil(blocks / 3)
-// tiles of 1 to 3 whole 128-row blocks (the first `extra` tiles one block taller).
+// Row-grouped kinds with block_m a multiple of 128: every segment is cut into
+// ceil(blocks / max_blk) tiles of whole 128-row blocks, as even as they come (the first `extra`
+// tiles one block taller), so no tile is taller than max_blk blocks.
 template <int KIND, bool GA>
 __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
@@ -1196,7 +1198,7 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
     for (int base = 0; base < G; base += 64) {
       const int g = base + lane;
       const int nb = g < G ? (p.seg[g + 1] - p.seg[g]) / kTallBlk : 0;
-      int x = (nb + kTallMaxBlk - 1) / kTallMaxBlk;
+      int x = (nb + p.max_blk - 1) / p.max_blk;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(x, o, 64);
@@ -1424,16 +1426,37 @@ hipError_t launch_kind(const GemmArgs& a, int64_t grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Tallest tile for a row-grouped launch of n_tiles_n column tiles over `rows` real rows in G
+// groups. The segment sizes live on the device, so the host prices an even split (rows / G per
+// group, rounded up to whole blocks): per choice of at most 3 or 2 blocks a tile, the number of
+// waves of 256 tiles times the tallest tile's cost. A 256-row tile does 2/3 of the work of a
+// 384-row one at a lower matrix-unit rate (about 1/1.1). The estimate is rough for skewed
+// routing, so 2 must win by a tenth. Few long segments choose it: 64 blocks x 16 column tiles
+// (a dense layer of 8192 tokens, N = 4096) make 352 tiles of 384 rows, 1.4 waves, or 512 tiles
+// of 256 rows, two whole waves.
+int tall_max_blk(int64_t rows, int G, int n_tiles_n) {
+  if (rows <= 0 || G <= 0) return kTallMaxBlk;
+  const int64_t nb = (rows + (int64_t)G * kTallBlk - 1) / ((int64_t)G * kTallBlk);   // >= 1
+  auto cost = [&](int mb) {
+    const int64_t per_g = (nb + mb - 1) / mb;                 // tiles of one group
+    const int64_t tallest = (nb + per_g - 1) / per_g;
+    const int64_t waves = (per_g * G * n_tiles_n + kPersistentWgs - 1) / kPersistentWgs;
+    return (double)waves * (double)tallest * (tallest >= 3 ? 1.0 : 1.1);
+  };
+  return cost(2) < 0.9 * cost(kTallMaxBlk) ? 2 : kTallMaxBlk;
+}
+
 // Row-grouped kinds: tall tiles for block_m % 128 == 0, 64-row tiles for block_m == 64, the
 // register-staged engine for 16 and 32.
 template <int KIND>
-hipError_t launch_rows(GemmArgs a, int64_t mcap, hipStream_t st) {
+hipError_t launch_rows(GemmArgs a, int64_t mcap, int64_t rows, hipStream_t st) {
   if (a.block_m % kTallBlk == 0) {
     if (a.seg == nullptr) return hipErrorInvalidValue;
     constexpr int cols = tile_cols<KIND>(kTall8BN);
     a.n_tiles_n = (int)((a.N + cols - 1) / cols);
-    // sum over groups of ceil(nb_g / 3) <= (sum nb_g + 2 G) / 3, sum nb_g <= mcap / 128
-    const int64_t tiles = (mcap / kTallBlk + 2 * (int64_t)a.G) / kTallMaxBlk + 1;
+    a.max_blk = tall_max_blk(rows, a.G, a.n_tiles_n);
+    // sum over groups of ceil(nb_g / mb) <= (sum nb_g + (mb - 1) G) / mb, sum nb_g <= mcap / 128
+    const int64_t tiles = (mcap / kTallBlk + (a.max_blk - 1) * (int64_t)a.G) / a.max_blk + 1;
     const int64_t grid = (tiles * a.n_tiles_n + kNumXcd - 1) / kNumXcd * kNumXcd;
     if constexpr (KIND == kFwdGateUp) {
       if (a.a_rows) {
@@ -1476,6 +1499,7 @@ hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
   g.block_m = s.block_m;
   g.I = s.I;
   g.G = s.E + s.S;
+  const int64_t rows = (int64_t)s.T * (s.K + s.S);   // real (unpadded) permuted rows
   g.seg = seg_offsets;
   g.tile_group = tile_group;
   g.total_rows = total_rows;
@@ -1488,7 +1512,7 @@ hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
   g.out = a; g.ldo = s.I; g.out2 = h_save;
   g.N = s.I; g.K = s.H;
   if (which & MOE_FWD_GATEUP) {
-    hipError_t e = launch_rows<kFwdGateUp>(g, mcap, st);
+    hipError_t e = launch_rows<kFwdGateUp>(g, mcap, rows, st);
     if (e != hipSuccess) return e;
   }
   if (!(which & MOE_FWD_DOWN)) return hipSuccess;
@@ -1498,7 +1522,7 @@ hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
   g.b = w2; g.ldb = s.I; g.b_gstride = (int64_t)s.H * s.I;
   g.out = y_perm; g.ldo = s.H; g.out2 = nullptr;
   g.N = s.H; g.K = s.I;
-  return launch_rows<kFwdDown>(g, mcap, st);
+  return launch_rows<kFwdDown>(g, mcap, rows, st);
 }
 
 hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap,
@@ -1510,6 +1534,7 @@ hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap
   g.block_m = s.block_m;
   g.I = s.I;
   g.G = s.E + s.S;
+  const int64_t rows = (int64_t)s.T * (s.K + s.S);   // real (unpadded) permuted rows
   g.seg = seg_offsets;
   g.tile_group = tile_group;
   g.total_rows = total_rows;
@@ -1519,7 +1544,7 @@ hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap
   g.aux = h_save; g.out = dh;
   g.N = s.I; g.K = s.H;
   if (which & MOE_DGRAD_DOWN) {
-    hipError_t e = launch_rows<kDgradDown>(g, mcap, st);
+    hipError_t e = launch_rows<kDgradDown>(g, mcap, rows, st);
     if (e != hipSuccess) return e;
   }
   if (!(which & MOE_DGRAD_GATEUP)) return hipSuccess;
@@ -1528,7 +1553,7 @@ hipError_t launch_ggemm_dgrad(const moe_shape_t& s, uint32_t which, int64_t mcap
   g.b = w1; g.ldb = s.H; g.b_gstride = (int64_t)2 * s.I * s.H;
   g.aux = nullptr; g.out = dx_perm; g.ldo = s.H;
   g.N = s.H; g.K = 2 * s.I;
-  return launch_rows<kDgradGateUp>(g, mcap, st);
+  return launch_rows<kDgradGateUp>(g, mcap, rows, st);
 }
 
 namespace {
