@@ -237,6 +237,9 @@ def _compare_layer(buf, f, b):
     # from empty to 24 contraction stages: tiles chained and not chained within one workgroup
     (1500, 1024, 64, 4, 256, 1, 64, (3, 17, 40)),
     (1500, 1024, 64, 4, 256, 1, 128, (5,)),
+    # one wave of tiles, so the host caps tiles at two 128-row blocks: the shared expert's 9
+    # blocks split 2+2+2+2+1, a routed expert's 7 blocks 2+2+2+1
+    (1100, 256, 4, 2, 128, 1, 128, (2,)),
     # a dense SwiGLU FFN as one group (E = K = 1): one segment of every token, many row tiles
     (1000, 512, 1, 1, 1024, 0, 128, ()),
     (777, 256, 1, 1, 320, 0, 64, ()),
