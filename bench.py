@@ -15,7 +15,9 @@ assignment, so the selection kernel runs but decides nothing else.
 Other workloads (forward only, routing computed from x): `--workload c3` is the skewed full layer
 (T=16384, Zipf logit offsets, 2 shared experts, block 128); `--workload c5` is decode (T=256,
 random routing, 2 shared experts, block 16). `--workload dense` runs the default step on a dense
-SwiGLU FFN expressed as one group (E = K = 1, intermediate 11264).
+SwiGLU FFN expressed as one group (E = K = 1, intermediate 11264). `--workload ep8` runs it on one
+GPU's share of the default layer under 8-way expert parallelism: 16 local experts with 3072 rows
+each (8192 tokens top-6 over 16 experts; the exchange between GPUs is not part of it).
 
 Prints one JSON line. `value` is the useful grouped-GEMM TFLOP/s of the whole step (padding
 excluded). It also carries the dominant kernel's roofline, timed with HIP events on the launch
@@ -177,10 +179,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("c2", "c3", "c5", "dense"), default="c2",
+    ap.add_argument("--workload", choices=("c2", "c3", "c5", "dense", "ep8"), default="c2",
                     help="c2: forward+backward at the uniform 8192-token shape (default); c3: skewed "
                          "16384-token full layer forward; c5: 256-token decode forward; dense: "
-                         "forward+backward of a dense SwiGLU FFN (intermediate 11264) as one group")
+                         "forward+backward of a dense SwiGLU FFN (intermediate 11264) as one group; "
+                         "ep8: forward+backward of one GPU's 16-expert share under 8-way expert "
+                         "parallelism (3072 rows per expert)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, copy a cold buffer of this many MiB (a plain copy of known "
                          "size that scales the HBM byte counters)")
@@ -209,7 +213,7 @@ def main():
     log(f"[bench] {args.workload}: generating inputs T={T} H={H} E={E} K={K} I={I} S={S} B={B}")
     t0 = time.perf_counter()
     x, w1, w2 = Sy.draw_x(cfg), Sy.draw_w1_all(cfg), Sy.draw_w2_all(cfg)
-    fwd_bwd = args.workload in ("c2", "dense")
+    fwd_bwd = args.workload in ("c2", "dense", "ep8")
     if fwd_bwd:
         dy, logits = Sy.draw_dy(cfg), Sy.uniform_logits(cfg)
     else:
@@ -336,6 +340,9 @@ def main():
                      "intermediate=11264, block_m=128)",
             "c2": "grouped-GEMM MoE FFN forward+backward, uniform routing (T=8192, hidden=4096, "
                   "128 experts top-6, intermediate=1408, block_m=128, 384 rows per expert)",
+            "ep8": "one GPU's share of the 128-expert layer under 8-way expert parallelism, "
+                   "forward+backward: 16 experts x 3072 rows (T=8192 top-6 uniform over 16 "
+                   "experts, hidden=4096, intermediate=1408, block_m=128)",
             "c3": "MoE FFN full layer forward from x, skewed routing (T=16384, hidden=4096, 128 "
                   "experts top-6 with Zipf(1.1) logit offsets + 2 shared experts, intermediate=1408, "
                   "block_m=128)",
@@ -406,7 +413,7 @@ def main():
             "this_library_fwd_gateup_ms": round(stage_ms["fwd_gateup"], 4)}
         del W1t
     sample = args.cpu_sample if args.cpu_sample is not None else {"c2": 384, "c3": 256, "dense": 8192,
-                                                                   "c5": 256}[args.workload]
+                                                                   "c5": 256, "ep8": 384}[args.workload]
     if sample > 0:
         log(f"[bench] CPU oracle on {sample} tokens")
         out["cpu_baseline"] = (cpu_baseline_fwd_bwd(cfg, x, w1, w2, logits, dy, sample) if fwd_bwd

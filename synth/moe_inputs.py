@@ -77,6 +77,11 @@ CONFIGS = {
     # its width; the reading is the active experts' total width per token, 8 x 1408 = 11264.
     "dense": MoEConfig("dense", T=8192, H=4096, E=1, K=1, I=11264, S=0, block_m=128, seed=0,
                        routing="uniform"),
+    # One GPU's share of c2 under 8-way expert parallelism: its 16 local experts receive
+    # 8 x 8192 x 6 / 128 = 3072 rows each, modelled as 8192 local tokens routed top-6 uniformly
+    # over the 16 experts (the GEMMs see exactly that shape; the exchange itself is not modelled).
+    "ep8": MoEConfig("ep8", T=8192, H=4096, E=16, K=6, I=1408, S=0, block_m=128, seed=0,
+                     routing="uniform"),
     # Decode with 16 experts forced empty by a -10 selection bias (empty-group skipping).
     "c5e": MoEConfig("c5e", T=256, H=4096, E=128, K=6, I=1408, S=2, block_m=16, seed=7,
                      routing="router", sel_bias="forced_empty",

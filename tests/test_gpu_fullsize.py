@@ -85,7 +85,20 @@ def _check_maps_exact(buf, idx, cfg):
 
 def test_uniform_8192_tokens_forward_and_backward():
     """Bench workload: T=8192, hidden 4096, 128 experts top-6, intermediate 1408, block 128."""
-    cfg = get_config("c2")
+    _uniform_layer(get_config("c2"), wgrad_groups=(0, 77, 127))
+
+
+def test_expert_parallel_share_forward_and_backward():
+    """One GPU's share of the bench layer under 8-way expert parallelism: 16 local experts with
+    3072 rows each (8192 tokens top-6 over 16 experts), so each weight-gradient tile contracts
+    over 48 stages of 64 rows."""
+    _uniform_layer(get_config("ep8"), wgrad_groups=(5,), per_group=4)
+
+
+def _uniform_layer(cfg, wgrad_groups, per_group=3):
+    """Forward and backward at a uniformly routed full-size shape: exact routing and maps,
+    sampled rows through the FFN, the combine and the dgrad, and the whole weight gradients of
+    wgrad_groups (the oracle runs their full segments)."""
     log(f"full size: {cfg}")
     s = M.make_shape(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.S, cfg.block_m)
     x, dy, logits = draw_x(cfg), draw_dy(cfg), uniform_logits(cfg)
@@ -103,7 +116,7 @@ def test_uniform_8192_tokens_forward_and_backward():
     np.testing.assert_array_equal(bits_host(buf["x_perm"][:total]), x[rt[:total]])
     # sampled permuted rows through the expert FFN
     rng = np.random.default_rng(0)
-    rows = _sample_rows(seg, rng)
+    rows = _sample_rows(seg, rng, per_group=per_group)
     h_ref, a_ref, y_ref = _oracle_rows(rows, seg, rt, x, cfg, lambda g: w1[g], lambda g: w2[g])
     R = torch.from_numpy(rows).to(DEV)
     assert_bf16_close(vals_host(buf["h_save"][R]), O.round_bf16(h_ref), "h_save rows")
@@ -149,8 +162,8 @@ def test_uniform_8192_tokens_forward_and_backward():
     assert_bf16_close(vals_host(buf["dy_perm"][R]), dyp_ref, "dy_perm rows")
     assert_bf16_close(vals_host(buf["dh"][R]), dh_ref, "dh rows")
     assert_bf16_close(vals_host(buf["dx_perm"][R]), dx_ref, "dx_perm rows")
-    # wgrad: whole dW of three experts (the oracle runs their full segments)
-    for g in (0, 77, 127):
+    # wgrad: whole dW of the chosen experts (the oracle runs their full segments)
+    for g in wgrad_groups:
         r0, r1 = int(seg[g]), int(seg[g + 1])
         seg_rows = np.arange(r0, r1)
         hg, ag, yg = _oracle_rows(seg_rows, seg, rt, x, cfg, lambda q: w1[q], lambda q: w2[q])
