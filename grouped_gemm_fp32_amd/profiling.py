@@ -4,6 +4,7 @@
     python -m grouped_gemm_fp32_amd.profiling traffic <fetch_dir> <write_dir> --calib-mib N \
         [--workload NAME] [--json OUT]
     python -m grouped_gemm_fp32_amd.profiling mfma <counter_dir>
+    python -m grouped_gemm_fp32_amd.profiling units <lds_counter_dir> <ta_counter_dir>
 
 `stats` prints the per-kernel table (calls, average and total duration, share of GPU time).
 `traffic` reads two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs (KiB per dispatch) of
@@ -15,6 +16,12 @@ dispatch id in the WRITE_SIZE run), and reports HBM bytes per launch.
 reports, per kernel, the matrix instructions per launch, the fraction of SIMD cycles the matrix
 unit was busy, and the shader clock the launch ran at (GRBM_GUI_ACTIVE sums the busy cycles of
 every XCD; dividing by the XCD count and by the dispatch's duration gives the clock).
+`units` reads a run of `SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE` and one of
+`TA_TA_BUSY SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE` and reports, per kernel, the share of
+all CU cycles in which LDS served indexed (non-DMA) accesses, the share stalled by bank conflicts,
+the share in which the texture addresser (the front of the vector memory path, which the
+direct-to-LDS loads and the stores share) was busy, and the share of wavefront cycles spent
+waiting for LDS results.
 """
 from __future__ import annotations
 
@@ -194,6 +201,49 @@ def mfma_table(path: str) -> str:
     return "\n".join(rows)
 
 
+N_CU = 256
+
+
+def _per_dispatch(path: str) -> dict:
+    disp = collections.defaultdict(dict)
+    for r in counter_rows(path):
+        d = disp[(short_name(r["Kernel_Name"]), int(r["Dispatch_Id"]))]
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return disp
+
+
+def unit_util(lds_path: str, ta_path: str) -> dict:
+    """Per kernel, means over its dispatches of: lds_active and lds_bank_conflict (fractions of
+    all CU cycles, the SQ_ counters summed over every CU), ta_busy (TA_TA_BUSY over all CU
+    cycles) and lds_wait (SQ_WAIT_INST_LDS over SQ_WAVE_CYCLES). A kernel missing from either run,
+    or a dispatch without GRBM_GUI_ACTIVE, is skipped."""
+    def means(path, need, f):
+        per = collections.defaultdict(list)
+        for (k, _), d in _per_dispatch(path).items():
+            if all(n in d for n in need) and d["GRBM_GUI_ACTIVE"] > 0:
+                per[k].append(f(d, d["GRBM_GUI_ACTIVE"] / N_XCD * N_CU) | {"us": d["_ns"] / 1e3})
+        return {k: {c: sum(e[c] for e in v) / len(v) for c in v[0]} for k, v in per.items()}
+    lds = means(lds_path, ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"),
+                lambda d, cu: {"lds_active": d["SQ_LDS_IDX_ACTIVE"] / cu,
+                               "lds_bank_conflict": d["SQ_LDS_BANK_CONFLICT"] / cu})
+    ta = means(ta_path, ("TA_TA_BUSY", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"),
+               lambda d, cu: {"ta_busy": d["TA_TA_BUSY"] / cu,
+                              "lds_wait": (d["SQ_WAIT_INST_LDS"] / d["SQ_WAVE_CYCLES"]
+                                           if d["SQ_WAVE_CYCLES"] > 0 else 0.0)})
+    return {k: lds[k] | {c: v for c, v in ta[k].items() if c != "us"} for k in lds if k in ta}
+
+
+def units_table(lds_path: str, ta_path: str) -> str:
+    rows = ["| kernel | stage | avg (us) | LDS active | LDS bank-conflict stall | TA busy "
+            "| wave cycles waiting on LDS |", "|---|---|---|---|---|---|---|"]
+    for k, e in sorted(unit_util(lds_path, ta_path).items(), key=lambda kv: -kv[1]["us"]):
+        rows.append(f"| {k} | {label(k)} | {e['us']:.1f} | {100 * e['lds_active']:.1f}% | "
+                    f"{100 * e['lds_bank_conflict']:.1f}% | {100 * e['ta_busy']:.1f}% | "
+                    f"{100 * e['lds_wait']:.1f}% |")
+    return "\n".join(rows)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -201,6 +251,9 @@ def main(argv=None):
     s.add_argument("csv")
     m = sub.add_parser("mfma")
     m.add_argument("dir")
+    u = sub.add_parser("units")
+    u.add_argument("lds_dir")
+    u.add_argument("ta_dir")
     t = sub.add_parser("traffic")
     t.add_argument("fetch")
     t.add_argument("write")
@@ -214,6 +267,9 @@ def main(argv=None):
         return
     if a.cmd == "mfma":
         print(mfma_table(a.dir))
+        return
+    if a.cmd == "units":
+        print(units_table(a.lds_dir, a.ta_dir))
         return
     tr = traffic(a.fetch, a.write, a.calib_mib)
     print(json.dumps(tr, indent=1))

@@ -78,3 +78,31 @@ def test_mfma_utilisation(tmp_path):
     assert e["us"] == pytest.approx(1.5)
     table = P.mfma_table(str(tmp_path / "m"))
     assert "fwd_gateup" in table and "1.6%" in table
+
+
+def test_unit_utilisation(tmp_path):
+    # 1000 cycles per XCD: 256 CUs give 256000 CU cycles; LDS serves indexed accesses in 64000 of
+    # them (25%), 2560 stalled by bank conflicts (1%); the TA is busy 128000 (50%); waves wait on
+    # LDS 300 of their 3000 cycles (10%)
+    lds = _write(tmp_path / "l", [
+        (3, TALL0, "SQ_LDS_IDX_ACTIVE", 64000.0, 0, 500),
+        (3, TALL0, "SQ_LDS_BANK_CONFLICT", 2560.0, 0, 500),
+        (3, TALL0, "GRBM_GUI_ACTIVE", 8 * 1000.0, 0, 500),
+        (4, GATHER, "SQ_LDS_IDX_ACTIVE", 0.0, 600, 700),       # not in the TA run: left out
+        (4, GATHER, "SQ_LDS_BANK_CONFLICT", 0.0, 600, 700),
+        (4, GATHER, "GRBM_GUI_ACTIVE", 800.0, 600, 700)])
+    ta = _write(tmp_path / "t", [
+        (3, TALL0, "TA_TA_BUSY", 128000.0, 0, 500),
+        (3, TALL0, "SQ_WAIT_INST_LDS", 300.0, 0, 500),
+        (3, TALL0, "SQ_WAVE_CYCLES", 3000.0, 0, 500),
+        (3, TALL0, "GRBM_GUI_ACTIVE", 8 * 1000.0, 0, 500)])
+    u = P.unit_util(lds, ta)
+    assert set(u) == {"ggemm_tall8_kernel<0,false>"}
+    e = u["ggemm_tall8_kernel<0,false>"]
+    assert e["lds_active"] == pytest.approx(0.25)
+    assert e["lds_bank_conflict"] == pytest.approx(0.01)
+    assert e["ta_busy"] == pytest.approx(0.5)
+    assert e["lds_wait"] == pytest.approx(0.1)
+    assert e["us"] == pytest.approx(0.5)
+    table = P.units_table(lds, ta)
+    assert "fwd_gateup" in table and "| 25.0% | 1.0% | 50.0% | 10.0% |" in table
