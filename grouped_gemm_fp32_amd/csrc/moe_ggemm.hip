@@ -450,9 +450,14 @@ constexpr uint32_t kPastEnd = 0x80000000u;
 // Issued from asm: the instruction has no register result (it writes LDS through M0), and hiding
 // it from the compiler keeps it from draining every DMA before unrelated LDS reads; the kernel's
 // own vmcnt waits and barriers order the data.
+// M0 is a reserved register, so the compiler would not honour it in a clobber list: the block
+// saves and restores it. On GFX9-family hardware an LDS DMA that reads M0 right after a scalar
+// write of M0 needs one wait state in between, hence the s_nop.
 __device__ __forceinline__ void dma16(v4u32_t r, uint32_t voff, uint32_t lds_wave) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(uniform(lds_wave)), "v"(voff), "s"(r) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+               "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(uniform(lds_wave)), "v"(voff), "s"(r) : "memory");
 }
 
 // Waits, each also a compiler memory barrier so that no LDS access moves across them.
