@@ -796,9 +796,12 @@ __device__ __forceinline__ void stage_bf16(unsigned char* scr, int lane, Val val
   }
 }
 
-// The same for fp32 values: dst(row, col, float4) gets 4 consecutive columns.
-template <int NJ, class Val, class Dst>
-__device__ __forceinline__ void stage_f32(unsigned char* scr, int lane, Val val, Dst dst) {
+// The same for fp32 values: dst(it, row, col, float4) gets 4 consecutive columns of row chunk it.
+// The chunks go in batches of B: pre(it, row, col) runs for each chunk of a batch before the
+// batch's first dst(), so the loads it issues are in flight together (a dst() that stores would
+// otherwise keep the next chunk's loads behind it).
+template <int NJ, int B, class Val, class Pre, class Dst>
+__device__ __forceinline__ void stage_f32_pre(unsigned char* scr, int lane, Val val, Pre pre, Dst dst) {
   constexpr int W = NJ * 32, NCH = W / 4, RS = W * 4, RPI = 64 / NCH;
   static_assert(NCH >= 4 && NCH <= 64 && (NCH & (NCH - 1)) == 0, "row chunks");
   const int r = lane & 31, hi = lane >> 5;
@@ -810,12 +813,25 @@ __device__ __forceinline__ void stage_f32(unsigned char* scr, int lane, Val val,
       const float4 w = make_float4(val(j, q, 0), val(j, q, 1), val(j, q, 2), val(j, q, 3));
       *reinterpret_cast<float4*>(scr + r * RS + ((ch ^ (r & (NCH - 1))) * 16)) = w;
     }
+  static_assert((32 / RPI) % B == 0, "whole batches");
 #pragma unroll
-  for (int it = 0; it < 32 / RPI; ++it) {
-    const int rr = it * RPI + lane / NCH, c = lane % NCH;
-    const float4 d = *reinterpret_cast<const float4*>(scr + rr * RS + ((c ^ (rr & (NCH - 1))) * 16));
-    dst(rr, c * 4, d);
+  for (int i0 = 0; i0 < 32 / RPI; i0 += B) {
+#pragma unroll
+    for (int it = i0; it < i0 + B; ++it) pre(it, it * RPI + lane / NCH, (lane % NCH) * 4);
+#pragma unroll
+    for (int it = i0; it < i0 + B; ++it) {
+      const int rr = it * RPI + lane / NCH, c = lane % NCH;
+      const float4 d = *reinterpret_cast<const float4*>(scr + rr * RS + ((c ^ (rr & (NCH - 1))) * 16));
+      dst(it, rr, c * 4, d);
+    }
   }
+}
+
+// stage_f32_pre without the pre step: dst(row, col, float4).
+template <int NJ, class Val, class Dst>
+__device__ __forceinline__ void stage_f32(unsigned char* scr, int lane, Val val, Dst dst) {
+  stage_f32_pre<NJ, 1>(scr, lane, val, [](int, int, int) {},
+                    [&](int, int rr, int c, float4 d) { dst(rr, c, d); });
 }
 
 __device__ __forceinline__ float4 bf4_to_f4(uint2 w) {
@@ -860,12 +876,21 @@ __device__ __forceinline__ void store_tile8(const GemmArgs& p, const f32x16_t (&
       for (int h = 0; h < TN / 2; ++h) {
       const int c0 = n0 + wn * WTN + h * 64;
       const int64_t ldh = 2 * (int64_t)p.I;
-      stage_f32<2>(scr, lane, [&](int j, int q, int e) { return acc[i][2 * h + j][4 * q + e]; },
-          [&](int rr, int c, float4 da) {
+      // the saved h of 4 row chunks at a time (half the 32 x 64 pass) is loaded before their
+      // first dh store: 8 loads in flight instead of 2, within the register budget
+      uint2 hg[8], hu[8];
+      stage_f32_pre<2, 4>(scr, lane, [&](int j, int q, int e) { return acc[i][2 * h + j][4 * q + e]; },
+          [&](int it, int rr, int c) {
+            const int64_t hrow = (mrow + rr) * ldh + c0 + c;
+            const bool in = c0 + c < p.N;
+            hg[it] = in ? *reinterpret_cast<const uint2*>(p.aux + hrow) : make_uint2(0, 0);
+            hu[it] = in ? *reinterpret_cast<const uint2*>(p.aux + hrow + p.I) : make_uint2(0, 0);
+          },
+          [&](int it, int rr, int c, float4 da) {
             if (c0 + c >= p.N) return;
             const int64_t hrow = (mrow + rr) * ldh + c0 + c;
-            const float4 gg = bf4_to_f4(*reinterpret_cast<const uint2*>(p.aux + hrow));
-            const float4 uu = bf4_to_f4(*reinterpret_cast<const uint2*>(p.aux + hrow + p.I));
+            const float4 gg = bf4_to_f4(hg[it]);
+            const float4 uu = bf4_to_f4(hu[it]);
             const float gv[4] = {gg.x, gg.y, gg.z, gg.w}, uv[4] = {uu.x, uu.y, uu.z, uu.w};
             const float av[4] = {da.x, da.y, da.z, da.w};
             float dg[4], du[4];
