@@ -186,6 +186,43 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 
 constexpr int64_t kSmallRowsBytes = 32ll << 20;   // activation bytes of a "small batch"
 
+// SwiGLU backward of one accumulator row for the small-tile engines: da -> dh = [da*u*s*(1 +
+// g(1-s)) | da*g*s] with g, u read from h_save (bf16). col(k) is the first of the 4 columns of
+// group k (at or past N: nothing to do), val(k, e) its da values. The h loads of all NG groups are
+// issued before the first dh store: the compiler cannot tell that h_save and dh do not overlap, so
+// a load after a store would wait for it.
+template <int NG, class Col, class Val>
+__device__ __forceinline__ void swiglu_bwd_row(const GemmArgs& p, int64_t m, Col col, Val val) {
+  const int64_t hrow = m * (2 * (int64_t)p.I);
+  uint2 gw[NG], uw[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int c = col(k);
+    const bool in = c < p.N;
+    gw[k] = in ? *reinterpret_cast<const uint2*>(p.aux + hrow + c) : make_uint2(0, 0);
+    uw[k] = in ? *reinterpret_cast<const uint2*>(p.aux + hrow + p.I + c) : make_uint2(0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int c = col(k);
+    if (c >= p.N) continue;
+    const float gg[4] = {lo_bf(gw[k].x), hi_bf(gw[k].x), lo_bf(gw[k].y), hi_bf(gw[k].y)};
+    const float uu[4] = {lo_bf(uw[k].x), hi_bf(uw[k].x), lo_bf(uw[k].y), hi_bf(uw[k].y)};
+    float dg[4], du[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = val(k, e);
+      const float sg = 1.0f / (1.0f + expf(-gg[e]));
+      dg[e] = v * uu[e] * sg * (1.0f + gg[e] * (1.0f - sg));
+      du[e] = v * gg[e] * sg;
+    }
+    *reinterpret_cast<uint2*>(p.out + hrow + c) =
+        make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
+    *reinterpret_cast<uint2*>(p.out + hrow + p.I + c) =
+        make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
+  }
+}
+
 template <int KIND, int BM, int BN, int MS, int WAVES_M>
 __global__ __launch_bounds__(kThreads, 2) void ggemm_kernel(GemmArgs p) {
   typedef KindTraits<KIND> Tr;
@@ -361,6 +398,13 @@ __global__ __launch_bounds__(kThreads, 2) void ggemm_kernel(GemmArgs p) {
       const int mloc = wm * WTM + i * MS + m_in;
       const int64_t m = m0 + mloc;
       if (!Tr::grouped_rows && m >= p.M) continue;
+      if constexpr (KIND == kDgradDown) {
+        constexpr int NQ = Mf::groups;
+        swiglu_bwd_row<TN * NQ>(p, m,
+            [&](int k) { return n0 + wn * WTN + (k / NQ) * MS + Mf::out_n(lane, k % NQ); },
+            [&](int k, int e) { return acc[i][k / NQ][4 * (k % NQ) + e]; });
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -370,28 +414,8 @@ __global__ __launch_bounds__(kThreads, 2) void ggemm_kernel(GemmArgs p) {
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-          if constexpr (KIND == kDgradDown) {
-            // da -> dh = [da*u*s*(1 + g(1-s)) | da*g*s] with g, u from h_save (bf16).
-            const int64_t hrow = m * (2 * (int64_t)p.I);
-            const uint2 gw = *reinterpret_cast<const uint2*>(p.aux + hrow + c);
-            const uint2 uw = *reinterpret_cast<const uint2*>(p.aux + hrow + p.I + c);
-            const float gg[4] = {lo_bf(gw.x), hi_bf(gw.x), lo_bf(gw.y), hi_bf(gw.y)};
-            const float uu[4] = {lo_bf(uw.x), hi_bf(uw.x), lo_bf(uw.y), hi_bf(uw.y)};
-            float dg[4], du[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float s = 1.0f / (1.0f + expf(-gg[e]));
-              dg[e] = v[e] * uu[e] * s * (1.0f + gg[e] * (1.0f - s));
-              du[e] = v[e] * gg[e] * s;
-            }
-            *reinterpret_cast<uint2*>(p.out + hrow + c) =
-                make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
-            *reinterpret_cast<uint2*>(p.out + hrow + p.I + c) =
-                make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
-          } else {
-            *reinterpret_cast<uint2*>(out + m * p.ldo + c) =
-                make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
-          }
+          *reinterpret_cast<uint2*>(out + m * p.ldo + c) =
+              make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
         }
     }
   }
@@ -515,6 +539,7 @@ __device__ __forceinline__ int kswz(int r, int c) {
 }
 
 // Epilogue shared by the engines: lane -> row, registers -> 4 consecutive columns per group.
+
 template <int KIND, int TM, int TN, int WTM, int WTN>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16_t (&acc)[TM][TN], int g,
                                            int m0, int n0, int wm, int wn, int lane) {
@@ -553,6 +578,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16_t (&a
     for (int i = 0; i < TM; ++i) {
       const int64_t m = m0 + wm * WTM + i * 32 + m_in;
       if (!Tr::grouped_rows && m >= p.M) continue;
+      if constexpr (KIND == kDgradDown) {
+        swiglu_bwd_row<TN * 4>(p, m,
+            [&](int k) { return n0 + wn * WTN + (k / 4) * 32 + Mf::out_n(lane, k % 4); },
+            [&](int k, int e) { return acc[i][k / 4][4 * (k % 4) + e]; });
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -562,27 +593,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const f32x16_t (&a
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-          if constexpr (KIND == kDgradDown) {
-            const int64_t hrow = m * (2 * (int64_t)p.I);
-            const uint2 gw = *reinterpret_cast<const uint2*>(p.aux + hrow + c);
-            const uint2 uw = *reinterpret_cast<const uint2*>(p.aux + hrow + p.I + c);
-            const float gg[4] = {lo_bf(gw.x), hi_bf(gw.x), lo_bf(gw.y), hi_bf(gw.y)};
-            const float uu[4] = {lo_bf(uw.x), hi_bf(uw.x), lo_bf(uw.y), hi_bf(uw.y)};
-            float dg[4], du[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float sg = 1.0f / (1.0f + expf(-gg[e]));
-              dg[e] = v[e] * uu[e] * sg * (1.0f + gg[e] * (1.0f - sg));
-              du[e] = v[e] * gg[e] * sg;
-            }
-            *reinterpret_cast<uint2*>(p.out + hrow + c) =
-                make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
-            *reinterpret_cast<uint2*>(p.out + hrow + p.I + c) =
-                make_uint2(pack_bf2(du[0], du[1]), pack_bf2(du[2], du[3]));
-          } else {
-            *reinterpret_cast<uint2*>(out + m * p.ldo + c) =
-                make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
-          }
+          *reinterpret_cast<uint2*>(out + m * p.ldo + c) =
+              make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
         }
     }
   }
