@@ -50,6 +50,49 @@ moe_status_t check_shape(const moe_shape_t* s) {
   return MOE_OK;
 }
 
+// The GEMM engines address their operands through buffer resources with 32-bit byte offsets,
+// and the weight-gradient stores and the gathering DMA mark masked lanes with an offset of 2^31
+// past the buffer's start. These checks reject every shape whose spans would not fit:
+//   - one group's expert weights, W1[g] = 2I x H bf16 (the larger of W1[g] and W2[g]);
+//   - one row tile of a row-grouped product, at most 384 rows of an operand up to max(H, 2I)
+//     wide;
+//   - (weight gradients) one segment's rows of an operand up to max(H, 2I) wide: a segment holds
+//     at most ceil(T/B)*B rows (each token picks distinct experts; shared segments hold T);
+//   - (weight gradients) one group's dW, which the 2^31 marker must lie past.
+constexpr int64_t kSpan32 = (int64_t)1 << 32;
+constexpr int64_t kMarker = (int64_t)1 << 31;
+constexpr int64_t kMaxTileRows = 384;
+
+moe_status_t check_gemm_spans(const moe_shape_t* s) {
+  const int64_t H = s->H, I = s->I, wide = H > 2 * I ? H : 2 * I;
+  if (4 * I * H >= kSpan32) {
+    set_err("an expert's W1 (2I x H bf16) must be smaller than 4 GiB: need I*H < 2^30");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (kMaxTileRows * wide * 2 >= kSpan32) {
+    set_err("a 384-row tile of a max(H, 2I)-wide bf16 operand must be smaller than 4 GiB");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+moe_status_t check_wgrad_spans(const moe_shape_t* s, int64_t dw_elem_bytes) {
+  const moe_status_t r = check_gemm_spans(s);
+  if (r != MOE_OK) return r;
+  const int64_t H = s->H, I = s->I, wide = H > 2 * I ? H : 2 * I, B = s->block_m;
+  const int64_t seg_rows = ((int64_t)s->T + B - 1) / B * B;
+  if (seg_rows * wide * 2 >= kSpan32) {
+    set_err("weight gradients: a segment of ceil(T/B)*B rows of a max(H, 2I)-wide bf16 operand "
+            "must be smaller than 4 GiB");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (2 * I * H * dw_elem_bytes > kMarker) {
+    set_err("weight gradients: one expert's dW1 (2I x H) must fit in 2^31 bytes");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
 int64_t capacity(const moe_shape_t* s) {
   const int64_t T = s->T, B = s->block_m;
   const int64_t R = T * s->K;
@@ -181,6 +224,10 @@ moe_status_t grouped_gemm_fwd(const moe_shape_t* s, uint32_t which, const uint16
     set_err("which must be a non-empty combination of MOE_FWD_GATEUP and MOE_FWD_DOWN");
     return MOE_ERR_INVALID_ARG;
   }
+  {
+    const moe_status_t r = check_gemm_spans(s);
+    if (r != MOE_OK) return r;
+  }
   if (s->T == 0) return MOE_OK;
   REQUIRE(seg_offsets);
   REQUIRE(tile_group);
@@ -212,9 +259,13 @@ moe_status_t grouped_gemm_fwd_gather(const moe_shape_t* s, uint32_t which, const
     return MOE_ERR_INVALID_ARG;
   }
   // the gathering DMA addresses x with 32-bit byte offsets and a past-the-end marker at 2^31
-  if ((int64_t)s->T * s->H * 2 > (int64_t)1 << 31) {
+  if ((int64_t)s->T * s->H * 2 > kMarker) {
     set_err("grouped_gemm_fwd_gather needs T*H*2 <= 2^31 bytes; use moe_permute + grouped_gemm_fwd");
     return MOE_ERR_UNSUPPORTED;
+  }
+  {
+    const moe_status_t r = check_gemm_spans(s);
+    if (r != MOE_OK) return r;
   }
   if (s->T == 0) return MOE_OK;
   REQUIRE(seg_offsets);
@@ -248,6 +299,10 @@ moe_status_t grouped_gemm_bwd(const moe_shape_t* s, uint32_t which, const uint16
   if (which == 0 || (which & ~(uint32_t)(MOE_DGRAD | MOE_WGRAD))) {
     set_err("which must be a non-empty combination of the MOE_DGRAD_* and MOE_WGRAD_* bits");
     return MOE_ERR_INVALID_ARG;
+  }
+  {
+    const moe_status_t r = (which & MOE_WGRAD) ? check_wgrad_spans(s, 2) : check_gemm_spans(s);
+    if (r != MOE_OK) return r;
   }
   const bool rows = s->T > 0;  // with T == 0 no activation row is read and dgrad is a no-op
   if (rows && (which & MOE_DGRAD)) {
@@ -304,6 +359,10 @@ moe_status_t grouped_gemm_wgrad_f32(const moe_shape_t* s, uint32_t which, const 
   if (which == 0 || (which & ~(uint32_t)MOE_WGRAD)) {
     set_err("which must be a non-empty combination of the MOE_WGRAD_* bits");
     return MOE_ERR_INVALID_ARG;
+  }
+  {
+    const moe_status_t r = check_wgrad_spans(s, 4);
+    if (r != MOE_OK) return r;
   }
   const bool rows = s->T > 0;
   REQUIRE(seg_offsets);

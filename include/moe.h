@@ -33,6 +33,14 @@
  *     Mcap = moe_row_capacity(shape) rows for every permuted buffer.
  *   - Supported: 1 <= K <= E, E <= 256, K <= 8, S <= 4, H % 128 == 0, I % 64 == 0,
  *     block_m in {16, 32, 64, 128, 256}.
+ *   - 32-bit spans: the GEMM kernels address each operand block with 32-bit byte offsets, so the
+ *     grouped_gemm_* calls return MOE_ERR_UNSUPPORTED (before any launch) unless
+ *       4*I*H < 2^32                       (one expert's W1, 2I x H bf16),
+ *       768*max(H, 2I) < 2^32              (a 384-row tile of the widest bf16 operand),
+ *     and, for the weight gradients (grouped_gemm_bwd with a WGRAD bit, grouped_gemm_wgrad_f32),
+ *       ceil(T/B)*B * 2*max(H, 2I) < 2^32  (the longest segment of the widest operand),
+ *       2I*H*e <= 2^31                     (one expert's dW1, e = 2 bytes bf16, 4 fp32).
+ *     grouped_gemm_fwd_gather also needs T*H*2 <= 2^31 (the rows of x it gathers from).
  */
 #ifndef MOE_H
 #define MOE_H

@@ -163,12 +163,17 @@ def select_topk(probs, sel_bias, K: int, normalize: bool = True):
     idx_all = np.broadcast_to(np.arange(E), (T, E))
     order = np.lexsort((idx_all, key_for_sort, nan), axis=1)
     topk_idx = order[:, :K].astype(np.int32)
-    sel_p = np.take_along_axis(p, topk_idx, axis=1).astype(np.float64)
-    if normalize:
-        w = sel_p / sel_p.sum(axis=1, keepdims=True)
-    else:
-        w = sel_p
-    return topk_idx, w.astype(np.float32)
+    return topk_idx, combine_weights(p, topk_idx, normalize)
+
+
+def combine_weights(probs, topk_idx, normalize: bool = True) -> np.ndarray:
+    """Weights of a given selection: w_j = p_{e_j} / sum_i p_{e_i} over the token's K selected
+    experts (renormalised) or w_j = p_{e_j}, from the affinities alone (TR section A2, load
+    balancing: the bias decides the selection only). float64, rounded once to fp32."""
+    p = np.asarray(probs, dtype=np.float32)
+    sel_p = np.take_along_axis(p, np.asarray(topk_idx, dtype=np.int64), axis=1).astype(np.float64)
+    w = sel_p / sel_p.sum(axis=1, keepdims=True) if normalize else sel_p
+    return w.astype(np.float32)
 
 
 def expert_counts(topk_idx, E: int) -> np.ndarray:

@@ -75,3 +75,37 @@ def assert_bf16_close(got, ref, name, tol=2e-2, row_axis=-1):
     far = np.abs(got - ref) > 2.0 ** -6 * np.abs(ref) + 2.0 ** -8 * rms
     assert far.mean() <= 1e-3, f"{name}: {far.sum()} elements ({far.mean():.2e}) off"
     log(f"  {name}: rel-L2 {r:.2e}, worst row {worst:.2e}, far {int(far.sum())}")
+
+
+def validated_routing(idx_gpu, probs_ref, sel_bias, K, delta=1e-6, normalize=True):
+    """The oracle's routing with every near-tied token taken as the GPU chose it, once that choice
+    is shown to be valid.
+
+    A token whose oracle margin between the K-th and (K+1)-th key is at least ``delta`` must match
+    the oracle exactly. Elsewhere the GPU's experts must be K distinct ones, each keyed within
+    ``delta`` of the oracle's K-th key, in slots whose keys do not increase by more than ``delta``.
+    Returns (idx, w, mism): the selection (the oracle's, with those valid alternatives), the
+    oracle's weights of that selection (the affinities p renormalised over the chosen experts),
+    and the mask of tokens that took an alternative. Every expected map and row of a test is then
+    built by the oracle from ``idx``."""
+    idx_gpu = np.asarray(idx_gpu)
+    key = O.selection_keys(probs_ref, sel_bias).astype(np.float64)
+    key = np.nan_to_num(key, nan=-np.inf)
+    ref_idx, _ = O.select_topk(probs_ref, sel_bias, K, normalize)
+    T, E = key.shape
+    srt = -np.sort(-key, axis=1)
+    margin = srt[:, K - 1] - (srt[:, K] if K < E else -np.inf)
+    mism = np.any(idx_gpu != ref_idx, axis=1)
+    assert not np.any(mism & (margin >= delta)), \
+        f"{int((mism & (margin >= delta)).sum())} tokens with a decided ranking differ"
+    for t in np.nonzero(mism)[0]:
+        row = idx_gpu[t]
+        assert np.all((row >= 0) & (row < E)) and len(set(row.tolist())) == K, (t, row)
+        chosen = key[t, row]
+        assert chosen.min() >= srt[t, K - 1] - delta, (t, row)
+        assert np.all(np.diff(chosen) <= delta), (t, row)
+    idx = ref_idx.copy()
+    idx[mism] = idx_gpu[mism]
+    log(f"  routing: {int(mism.sum())} of {T} tokens took a valid near-tie alternative "
+        f"({int((margin < delta).sum())} with margin < {delta})")
+    return idx, O.combine_weights(probs_ref, idx, normalize), mism

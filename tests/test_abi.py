@@ -292,3 +292,47 @@ def test_gather_forward_checks(lib):
     assert "2^31" in M.moe_last_error()
     empty = M.make_shape(0, 256, 8, 2, 128, 1, 16)
     assert lib.grouped_gemm_fwd_gather(ctypes.byref(empty), M.MOE_FWD, *([None] * 10), None) == 0
+
+
+def test_gemm_32bit_span_limits(lib):
+    """The GEMM engines address operands with 32-bit byte offsets (and mark masked lanes 2^31 past
+    a buffer's start): shapes whose spans do not fit are refused with MOE_ERR_UNSUPPORTED before
+    any launch, one case per span."""
+    d = ctypes.c_void_p(16)
+
+    def fwd(s):
+        return lib.grouped_gemm_fwd(ctypes.byref(s), M.MOE_FWD, *([d] * 9), None)
+
+    def gather(s):
+        return lib.grouped_gemm_fwd_gather(ctypes.byref(s), M.MOE_FWD, *([d] * 10), None)
+
+    def bwd(s, which):
+        return lib.grouped_gemm_bwd(ctypes.byref(s), which, *([d] * 13), None)
+
+    def wgrad32(s):
+        return lib.grouped_gemm_wgrad_f32(ctypes.byref(s), M.MOE_WGRAD, *([d] * 7), None)
+
+    # an expert's W1 (2I x H bf16) reaches 4 GiB: I*H = 2^30
+    s = M.make_shape(8, 32768, 8, 2, 32768, 0, 128)
+    for st in (fwd(s), gather(s), bwd(s, M.MOE_DGRAD), bwd(s, M.MOE_WGRAD), wgrad32(s)):
+        assert st == -2 and "4 GiB" in M.moe_last_error()
+    # ... one step below fits (T = 0: accepted, nothing launched)
+    ok = M.make_shape(0, 32768, 8, 2, 32704, 0, 128)
+    assert fwd(ok) == 0 and bwd(ok, M.MOE_DGRAD) == 0
+    # a 384-row tile of a max(H, 2I)-wide operand reaches 4 GiB (the weights alone would fit)
+    s = M.make_shape(8, 5592448, 8, 2, 64, 0, 128)
+    assert fwd(s) == -2 and "384-row tile" in M.moe_last_error()
+    assert bwd(s, M.MOE_DGRAD) == -2
+    # weight gradients: a segment of ceil(T/B)*B rows reaches 4 GiB (the forward is unaffected)
+    s = M.make_shape(262144, 8192, 8, 2, 64, 1, 128)
+    for st in (bwd(s, M.MOE_WGRAD_DOWN), bwd(s, M.MOE_WGRAD_GATEUP), wgrad32(s)):
+        assert st == -2 and "segment" in M.moe_last_error()
+    assert bwd(M.make_shape(0, 8192, 8, 2, 64, 1, 128), M.MOE_DGRAD) == 0
+    # weight gradients: one expert's bf16 dW1 exceeds 2^31 bytes (the 2^31 past-end marker)
+    s = M.make_shape(8, 32768, 8, 2, 16448, 0, 128)
+    assert bwd(s, M.MOE_WGRAD) == -2 and "2^31" in M.moe_last_error()
+    assert fwd(M.make_shape(0, 32768, 8, 2, 16448, 0, 128)) == 0
+    # ... and the fp32 dW1 of a shape whose bf16 dW1 still fits
+    s = M.make_shape(8, 16384, 8, 2, 16448, 0, 128)
+    assert wgrad32(s) == -2 and "2^31" in M.moe_last_error()
+    assert bwd(M.make_shape(0, 16384, 8, 2, 16448, 0, 128), M.MOE_DGRAD) == 0
