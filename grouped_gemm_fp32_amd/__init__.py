@@ -75,6 +75,7 @@ _SIGS = {
     "moe_workspace_size": (ctypes.c_size_t, [_SP]),
     "moe_route": (ctypes.c_int, [_SP] + [_P] * 10),
     "moe_permute": (ctypes.c_int, [_SP] + [_P] * 9 + [ctypes.c_size_t, _P]),
+    "moe_permute_noalloc": (ctypes.c_int, [_SP] + [_P] * 9),
     "grouped_gemm_fwd": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 10),
     "grouped_gemm_fwd_gather": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 11),
     "grouped_gemm_bwd": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 14),
@@ -235,6 +236,21 @@ def moe_permute(shape, topk_idx, x, seg_offsets, tile_group, total_rows, row_tok
         _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(tile_group, "tile_group", _i32()),
         _ptr(total_rows, "total_rows", _i32()), _ptr(row_token, "row_token", _i32()),
         _ptr(pos, "pos", _i32()), _ptr(x_perm, "x_perm", _bf16()), _ptr(ws, "ws"), ws_bytes, st))
+
+
+def moe_permute_noalloc(shape, topk_idx, x, seg_offsets, tile_group, total_rows, row_token, pos,
+                        x_perm, stream=None):
+    lib = load_library()
+    T, H, E, K, I, G, mcap = _dims(shape)
+    _need(shape, topk_idx=(topk_idx, T * K), x=(x, T * H), seg_offsets=(seg_offsets, G + 1),
+          tile_group=(tile_group, mcap // shape.block_m), total_rows=(total_rows, 1),
+          row_token=(row_token, mcap), pos=(pos, T * K), x_perm=(x_perm, mcap * H))
+    st = _stream(stream, topk_idx)
+    _check("moe_permute_noalloc", lib.moe_permute_noalloc(
+        ctypes.byref(shape), _ptr(topk_idx, "topk_idx", _i32()), _ptr(x, "x", _bf16()),
+        _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(tile_group, "tile_group", _i32()),
+        _ptr(total_rows, "total_rows", _i32()), _ptr(row_token, "row_token", _i32()),
+        _ptr(pos, "pos", _i32()), _ptr(x_perm, "x_perm", _bf16()), st))
 
 
 def grouped_gemm_fwd(shape, which, x_perm, seg_offsets, tile_group, total_rows, w1, w2, h_save, a,

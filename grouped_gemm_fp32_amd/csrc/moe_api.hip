@@ -3,6 +3,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -127,11 +129,85 @@ int64_t capacity(const moe_shape_t* s) {
     g_err[0] = 0;                            \
   } while (0)
 
+// moe_permute with T == 0: still define the (empty) segments, so later calls see G+1 zero offsets
+// and no rows.
+moe_status_t permute_empty(const moe_shape_t* s, int32_t* seg_offsets, int32_t* total_rows,
+                           void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = moe::launch_fill_i32(seg_offsets, 0, s->E + s->S + 1, st);
+  if (e == hipSuccess) e = moe::launch_fill_i32(total_rows, 0, 1, st);
+  return hip_status(e, "moe_permute");
+}
+
+// moe_permute's pointer checks for T > 0 (the workspace aside).
+moe_status_t check_permute_args(const moe_shape_t* s, const int32_t* topk_idx, const uint16_t* x,
+                                int32_t* tile_group, int32_t* row_token, int32_t* pos,
+                                uint16_t* x_perm) {
+  (void)s;
+  REQUIRE(topk_idx);
+  REQUIRE(tile_group);
+  REQUIRE(row_token);
+  REQUIRE(pos);
+  if (x) {
+    REQUIRE_T(x);
+    REQUIRE_T(x_perm);
+  }
+  return MOE_OK;
+}
+
+// Fixed device scratch of moe_permute_noalloc: the permutation's per-token-block expert
+// histograms, at most 128 token blocks x 256 experts int32 (128 KiB) for every shape that
+// check_shape accepts. Each GPU the library runs on holds its own copy until the process ends.
+// Host code never uses the array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+constexpr size_t kScratchBytes = (size_t)128 * 256 * sizeof(int32_t);
+static __device__ __align__(256) int32_t scratch[kScratchBytes / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream` (which must be the current one).
+moe_status_t device_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "moe_permute_noalloc(hipGetDevice)");
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_status(e, "moe_permute_noalloc(hipStreamGetDevice)");
+    if (sdev != dev) {
+      snprintf(g_err, sizeof(g_err),
+               "moe_permute_noalloc: the stream belongs to device %d but device %d is current",
+               (int)sdev, dev);
+      return MOE_ERR_INVALID_ARG;
+    }
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_err("moe_permute_noalloc: device index beyond the library's table of 64");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "moe_permute_noalloc(hipGetSymbolAddress)");
+    if (!ptr) {
+      set_err("moe_permute_noalloc: hipGetSymbolAddress returned NULL");
+      return MOE_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 const char* moe_status_string(int32_t status) {
   switch (status) {
@@ -189,20 +265,10 @@ moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx, const ui
   CHECK_SHAPE(s);
   REQUIRE(seg_offsets);
   REQUIRE(total_rows);
-  if (s->T == 0) {
-    // Still define the (empty) segments so later calls see G+1 zero offsets and no rows.
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e = moe::launch_fill_i32(seg_offsets, 0, s->E + s->S + 1, st);
-    if (e == hipSuccess) e = moe::launch_fill_i32(total_rows, 0, 1, st);
-    return hip_status(e, "moe_permute");
-  }
-  REQUIRE(topk_idx);
-  REQUIRE(tile_group);
-  REQUIRE(row_token);
-  REQUIRE(pos);
-  if (x) {
-    REQUIRE_T(x);
-    REQUIRE_T(x_perm);
+  if (s->T == 0) return permute_empty(s, seg_offsets, total_rows, stream);
+  {
+    const moe_status_t r = check_permute_args(s, topk_idx, x, tile_group, row_token, pos, x_perm);
+    if (r != MOE_OK) return r;
   }
   REQUIRE(ws);
   if (ws_bytes < moe_workspace_size(s)) {
@@ -213,6 +279,32 @@ moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx, const ui
                                         total_rows, row_token, pos, x_perm, (int32_t*)ws,
                                         (hipStream_t)stream),
                     "moe_permute");
+}
+
+moe_status_t moe_permute_noalloc(const moe_shape_t* s, const int32_t* topk_idx, const uint16_t* x,
+                                 int32_t* seg_offsets, int32_t* tile_group, int32_t* total_rows,
+                                 int32_t* row_token, int32_t* pos, uint16_t* x_perm, void* stream) {
+  CHECK_SHAPE(s);
+  REQUIRE(seg_offsets);
+  REQUIRE(total_rows);
+  if (s->T == 0) return permute_empty(s, seg_offsets, total_rows, stream);
+  {
+    const moe_status_t r = check_permute_args(s, topk_idx, x, tile_group, row_token, pos, x_perm);
+    if (r != MOE_OK) return r;
+  }
+  if (moe_workspace_size(s) > kScratchBytes) {
+    set_err("moe_permute_noalloc: the shape needs more than the 128 KiB of fixed scratch");
+    return MOE_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  {
+    const moe_status_t r = device_scratch((hipStream_t)stream, &ws);
+    if (r != MOE_OK) return r;
+  }
+  return hip_status(moe::launch_permute(*s, capacity(s), topk_idx, x, seg_offsets, tile_group,
+                                        total_rows, row_token, pos, x_perm, (int32_t*)ws,
+                                        (hipStream_t)stream),
+                    "moe_permute_noalloc");
 }
 
 moe_status_t grouped_gemm_fwd(const moe_shape_t* s, uint32_t which, const uint16_t* x_perm,

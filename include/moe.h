@@ -139,6 +139,23 @@ moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_idx, cons
                          size_t ws_bytes, void* stream);
 
 /*
+ * moe_permute_noalloc — moe_permute without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid it).
+ * The per-token-block histograms go to a fixed 128 KiB array in the library's device memory
+ * (one per GPU, held until the process ends), which covers every supported shape; a shape
+ * needing more would get MOE_ERR_WORKSPACE. It calls no allocating routine. Outputs, arguments
+ * and errors are moe_permute's, bit for bit. The stream must belong to the current device (else
+ * MOE_ERR_INVALID_ARG); the first call on a device looks up that device's array. Every call on a
+ * GPU shares its array: calls that overlap on one GPU (concurrent streams, or host threads)
+ * race and must be serialised by the caller. No state carries over between calls (each fully
+ * rewrites the histograms before reading them).
+ */
+moe_status_t moe_permute_noalloc(const moe_shape_t* shape, const int32_t* topk_idx,
+                                 const uint16_t* x, int32_t* seg_offsets, int32_t* tile_group,
+                                 int32_t* total_rows, int32_t* row_token, int32_t* pos,
+                                 uint16_t* x_perm, void* stream);
+
+/*
  * grouped_gemm_fwd — every group's SwiGLU FFN on its segment (TR section A2 MoE paragraph; TR
  * section 3.2 grouped GEMM). Rows r < total_rows of group g = tile_group[r/B]:
  *   MOE_FWD_GATEUP: h = x_perm[r] . w1[g]^T  (w1: [G, 2I, H]; rows 0..I-1 gate, I..2I-1 up),

@@ -336,3 +336,22 @@ def test_gemm_32bit_span_limits(lib):
     s = M.make_shape(8, 16384, 8, 2, 16448, 0, 128)
     assert wgrad32(s) == -2 and "2^31" in M.moe_last_error()
     assert bwd(M.make_shape(0, 16384, 8, 2, 16448, 0, 128), M.MOE_DGRAD) == 0
+
+
+def test_noalloc_permute_host_checks(lib):
+    """moe_permute_noalloc validates like moe_permute (no workspace argument) before any HIP call."""
+    s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
+    d, odd = ctypes.c_void_p(16), ctypes.c_void_p(24)
+    full = [d] * 8   # topk_idx, x, seg_offsets, tile_group, total_rows, row_token, pos, x_perm
+    for i in (0, 2, 3, 4, 5, 6):
+        a = list(full)
+        a[i] = None
+        assert lib.moe_permute_noalloc(ctypes.byref(s), *a, None) == -1, i
+        assert "NULL" in M.moe_last_error()
+    for i in (1, 7):
+        a = list(full)
+        a[i] = odd
+        assert lib.moe_permute_noalloc(ctypes.byref(s), *a, None) == -1, i
+        assert "aligned" in M.moe_last_error()
+    bad = M.make_shape(8, 256, 8, 9, 128, 1, 16)
+    assert lib.moe_permute_noalloc(ctypes.byref(bad), *full, None) == -1
