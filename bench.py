@@ -12,18 +12,21 @@ It uses T=8192 tokens, hidden 4096, 128 experts top-6, intermediate 1408, block 
 routing (every expert gets exactly 384 rows). The routing stage runs on logits that encode that
 assignment, so the selection kernel runs but decides nothing else.
 
-Other workloads (forward only, routing computed from x): `--workload c3` is the skewed full layer
-(T=16384, Zipf logit offsets, 2 shared experts, block 128); `--workload c5` is decode (T=256,
-random routing, 2 shared experts, block 16). `--workload dense` runs the default step on a dense
-SwiGLU FFN expressed as one group (E = K = 1, intermediate 11264). `--workload ep8` runs it on one
-GPU's share of the default layer under 8-way expert parallelism: 16 local experts with 3072 rows
-each (8192 tokens top-6 over 16 experts; the exchange between GPUs is not part of it).
+The default run also times, as sub-objects of the same line, the two forward workloads the metric
+names: `layer_c3`, the full MoE layer forward from x on the skewed 16384-token batch (router with
+Zipf logit offsets, 2 shared experts, block 128; tokens/s and the fraction of bf16 MFMA peak), and
+`decode_c5`, the 256-token decode forward (random routing, 2 shared experts, block 16; the weight
+stream as a fraction of HBM bandwidth). Both gather x's rows inside the gate/up product.
+
+Other workloads: `--workload c3` / `c5` make those forwards the main line; `--workload dense`
+runs the default step on a dense SwiGLU FFN expressed as one group (E = K = 1, intermediate
+11264); `--workload ep8` runs it on one GPU's share of the default layer under 8-way expert
+parallelism: 16 local experts with 3072 rows each (the exchange between GPUs is not part of it).
 
 Prints one JSON line. `value` is the useful grouped-GEMM TFLOP/s of the whole step (padding
 excluded). It also carries the dominant kernel's roofline, timed with HIP events on the launch
-stream, and the CPU oracle's throughput on a bounded sample of the same workload. With the default
-workload it also times, outside the step, the router backward on the step's routing (dlogits, then
-dWg and the router's share of dx in fp32) and the load-balancing bias update.
+stream, the shader clock read from the GPU's metrics over a few seconds of back-to-back steps
+after the timed ones, and the CPU oracle's throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -32,6 +35,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +45,22 @@ METRIC = "grouped-GEMM bf16 TFLOP/s (% MFMA peak) and MoE-layer tokens/s, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 (matrix and vector)
+NOMINAL_CLOCK_MHZ = 2400.0  # the clock the peaks above assume
+
+DESC = {
+    "dense": "dense SwiGLU FFN as one group, forward+backward (T=8192, hidden=4096, "
+             "intermediate=11264, block_m=128)",
+    "c2": "grouped-GEMM MoE FFN forward+backward, uniform routing (T=8192, hidden=4096, "
+          "128 experts top-6, intermediate=1408, block_m=128, 384 rows per expert)",
+    "ep8": "one GPU's share of the 128-expert layer under 8-way expert parallelism, "
+           "forward+backward: 16 experts x 3072 rows (T=8192 top-6 uniform over 16 "
+           "experts, hidden=4096, intermediate=1408, block_m=128)",
+    "c3": "MoE FFN full layer forward from x, skewed routing (T=16384, hidden=4096, 128 "
+          "experts top-6 with Zipf(1.1) logit offsets + 2 shared experts, intermediate=1408, "
+          "block_m=128)",
+    "c5": "MoE FFN decode forward from x, random routing (T=256, hidden=4096, 128 experts "
+          "top-6 + 2 shared experts, intermediate=1408, block_m=16)",
+}
 
 
 def log(msg):
@@ -78,23 +98,114 @@ def _threads():
     return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
 
 
-def cpu_baseline_fwd_bwd(cfg, x, w1, w2, logits, dy, sample_tokens):
-    """The CPU oracle, as it is, on the first `sample_tokens` tokens of the workload (fwd + bwd)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """The GPU's shader (GFX) clock while a workload runs back to back, through amdsmi's GPU
+    metrics. The firmware refreshes them about once a second, so a summary needs a window of a few
+    seconds: only readings the firmware published after the window opened count, averaged over the
+    8 XCDs. summary() is None where amdsmi, the metrics or fresh readings are unavailable."""
+
+    def __init__(self, period=0.05):
+        self.period, self.samples, self._stop, self._th, self._h = period, [], None, None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+        except Exception:   # no amdsmi, no device access: no clock in the line
+            self._h = None
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [float(c) for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))]
+        if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
+            clks = [float(m["current_gfxclk"])]
+        return m.get("system_clock_counter"), clks
+
+    def _run(self):
+        first, seen = None, set()
+        while not self._stop.is_set():
+            try:
+                stamp, clks = self._read()
+                if first is None:
+                    first = stamp          # published before the window opened: not counted
+                elif stamp != first and stamp not in seen and clks:
+                    seen.add(stamp)
+                    self.samples.append(sum(clks) / len(clks))
+            except Exception:
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._h is not None:
+            self.samples, self._stop = [], threading.Event()
+            self._th = threading.Thread(target=self._run, daemon=True)
+            self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._th is not None:
+            self._stop.set()
+            self._th.join()
+            self._th = None
+
+    def summary(self):
+        s = sorted(v for v in self.samples if v > 0)
+        if not s:
+            return None
+        return {"median_mhz": s[len(s) // 2], "min_mhz": s[0], "max_mhz": s[-1], "samples": len(s),
+                "source": "amdsmi GPU metrics (mean over the 8 XCDs of each once-a-second "
+                          "firmware reading) during a window of back-to-back steps after timing"}
+
+
+def sample_clock(torch, clock, step, seconds=3.0):
+    """Run `step` back to back for about `seconds` under the clock sampler; its summary."""
+    if clock is None or clock._h is None:
+        return None
+    with clock:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
+    return clock.summary()
+
+
+def cpu_baseline_fwd_bwd(cfg, x, w1, w2, logits, dy, stride):
+    """The CPU oracle, as it is, on one token in `stride` of the uniformly routed workload,
+    forward + backward. With stride 8 (or 16, 32) the sampled tokens route to 48 (24, 12) experts
+    with exactly 128 rows each, one whole block: the sample has no padding rows."""
+    import numpy as np
     from oracle import moe_oracle as O
 
-    T = sample_tokens
-    probs = O.softmax_probs(logits[:T])
+    sel = np.arange(0, cfg.T, stride)
+    T = len(sel)
+    probs = O.softmax_probs(logits[sel])
     kw = dict(T=T, H=cfg.H, E=cfg.E, K=cfg.K, I=cfg.I, S=cfg.S)
     t0 = time.perf_counter()
-    f = O.moe_forward(x[:T], w1, w2, B=cfg.block_m, probs=probs, **kw)
-    O.moe_backward(f, dy[:T], w1, w2, **kw)
+    f = O.moe_forward(x[sel], w1, w2, B=cfg.block_m, probs=probs, **kw)
+    O.moe_backward(f, dy[sel], w1, w2, **kw)
     dt = time.perf_counter() - t0
     rows = T * cfg.K + cfg.S * T
+    padded = int(f["total_rows"])
     flops = 18.0 * cfg.H * cfg.I * rows
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"first {T} tokens of the workload ({rows} expert rows), forward + backward, "
-                      f"float64 NumPy oracle; useful FLOPs / oracle seconds"}
+            "cpu_model": cpu_model(), "seconds": round(dt, 3), "rows_useful": rows,
+            "rows_padded": padded, "padded_over_useful": round(padded / rows, 4),
+            "sample": f"one token in {stride} of the workload ({T} tokens, {rows} expert rows, "
+                      f"{padded} after padding), forward + backward, float64 NumPy oracle; useful "
+                      f"FLOPs / oracle seconds"}
 
 
 def cpu_baseline_fwd(cfg, x, w1, w2, wg, logit_bias, sel_bias, sample_tokens):
@@ -104,15 +215,18 @@ def cpu_baseline_fwd(cfg, x, w1, w2, wg, logit_bias, sel_bias, sample_tokens):
     T = sample_tokens
     kw = dict(T=T, H=cfg.H, E=cfg.E, K=cfg.K, I=cfg.I, S=cfg.S)
     t0 = time.perf_counter()
-    O.moe_forward(x[:T], w1, w2, B=cfg.block_m, w_gate=wg, logit_bias=logit_bias,
-                  sel_bias=sel_bias, **kw)
+    f = O.moe_forward(x[:T], w1, w2, B=cfg.block_m, w_gate=wg, logit_bias=logit_bias,
+                      sel_bias=sel_bias, **kw)
     dt = time.perf_counter() - t0
     rows = T * cfg.K + cfg.S * T
+    padded = int(f["total_rows"])
     flops = 6.0 * cfg.H * cfg.I * rows
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"first {T} tokens of the workload ({rows} expert rows), forward from x, "
-                      f"float64 NumPy oracle; useful grouped-GEMM FLOPs / oracle seconds"}
+            "cpu_model": cpu_model(), "seconds": round(dt, 3), "rows_useful": rows,
+            "rows_padded": padded, "padded_over_useful": round(padded / rows, 4),
+            "sample": f"first {T} tokens of the workload ({rows} expert rows, {padded} after "
+                      f"padding), forward from x, float64 NumPy oracle; useful grouped-GEMM FLOPs "
+                      f"/ oracle seconds"}
 
 
 def _time_steps(torch, np, step, nstages, steps, warmup):
@@ -174,104 +288,141 @@ def router_backward_timing(torch, np, M, Sy, cfg, s, b, X, dev, reps=20):
             "balance_loss_ms": round(t_bal, 4)}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("c2", "c3", "c5", "dense", "ep8"), default="c2",
-                    help="c2: forward+backward at the uniform 8192-token shape (default); c3: skewed "
-                         "16384-token full layer forward; c5: 256-token decode forward; dense: "
-                         "forward+backward of a dense SwiGLU FFN (intermediate 11264) as one group; "
-                         "ep8: forward+backward of one GPU's 16-expert share under 8-way expert "
-                         "parallelism (3072 rows per expert)")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="before warmup, copy a cold buffer of this many MiB (a plain copy of known "
-                         "size that scales the HBM byte counters)")
-    ap.add_argument("--materialize", action="store_true",
-                    help="c3/c5: write x_perm in moe_permute and run grouped_gemm_fwd on it instead "
-                         "of gathering x's rows inside the gate/up product")
-    ap.add_argument("--cpu-sample", type=int, default=None,
-                    help="tokens of the workload the CPU oracle runs (0 = skip the CPU baseline); "
-                         "default 384 for c2, 256 for c3, all 256 for c5")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): the library "
-              f"implements the single-GPU path only; sharding the experts across GPUs (an "
-              f"all-to-all of the permuted rows each way) is not implemented.", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-    import grouped_gemm_fp32_amd as M
-    import synth as Sy
-
-    dev = "cuda:0"
-    cfg = Sy.get_config(args.workload)
+# ------------------------------------------------------------------------------------------------
+# forward from x (the skewed full layer, the decode)
+# ------------------------------------------------------------------------------------------------
+def run_forward(torch, np, M, Sy, name, W1, W2, dev, steps, warmup, materialize=False, clock=None):
+    """Time the forward from x of workload `name` (router, permutation, gate/up, down, combine).
+    W1/W2 are the device weights [G, 2I, H] / [G, H, I] (the workload's own draw). Returns the
+    measurement dict; the useful FLOPs exclude padding rows."""
+    cfg = Sy.get_config(name)
     T, H, E, K, I, S, B = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.S, cfg.block_m
-    log(f"[bench] {args.workload}: generating inputs T={T} H={H} E={E} K={K} I={I} S={S} B={B}")
-    t0 = time.perf_counter()
-    x, w1, w2 = Sy.draw_x(cfg), Sy.draw_w1_all(cfg), Sy.draw_w2_all(cfg)
-    fwd_bwd = args.workload in ("c2", "dense", "ep8")
-    if fwd_bwd:
-        dy, logits = Sy.draw_dy(cfg), Sy.uniform_logits(cfg)
-    else:
-        wg, lb, sb = Sy.draw_wg(cfg), Sy.draw_logit_bias(cfg), Sy.draw_sel_bias(cfg)
-    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
+    x, wg, lb, sb = Sy.draw_x(cfg), Sy.draw_wg(cfg), Sy.draw_logit_bias(cfg), Sy.draw_sel_bias(cfg)
     s = M.make_shape(T, H, E, K, I, S, B)
-    b = M.alloc_buffers(s, dev, backward=fwd_bwd, save_h=fwd_bwd)
-    X, W1, W2 = _bf(np, torch, x, dev), _bf(np, torch, w1, dev), _bf(np, torch, w2, dev)
-    if fwd_bwd:
-        DY, LG = _bf(np, torch, dy, dev), torch.from_numpy(logits).to(dev)
-        route_args = (None, None, None, None, LG)
-    else:
-        WG = torch.from_numpy(wg).to(dev)
-        LB = torch.from_numpy(lb).to(dev) if lb is not None else None
-        SB = torch.from_numpy(sb).to(dev)
-        route_args = (X, WG, LB, SB, b["logits"])
-    torch.cuda.synchronize()
-
-    # Forward-only workloads gather x's rows inside the gate/up product (no x_perm); the training
-    # step keeps x_perm, which the gate/up weight gradient reads.
-    gather = not fwd_bwd and not args.materialize
+    b = M.alloc_buffers(s, dev, backward=False, save_h=False)
+    X = _bf(np, torch, x, dev)
+    WG = torch.from_numpy(wg).to(dev)
+    LB = torch.from_numpy(lb).to(dev) if lb is not None else None
+    SB = torch.from_numpy(sb).to(dev)
+    gather = not materialize
     if gather:
         del b["x_perm"]
     stages = ["route", "permute", "fwd_gateup", "fwd_down", "combine"]
-    if fwd_bwd:
-        stages += ["combine_bwd", "dgrad_down", "dgrad_gateup", "wgrad_down", "wgrad_gateup",
-                   "unpermute_bwd"]
-    h_save = b.get("h_save")
 
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record()
         mark(0)
-        M.moe_route(s, *route_args, b["probs"], b["topk_idx"], b["topk_w"], b["expert_counts"])
+        M.moe_route(s, X, WG, LB, SB, b["logits"], b["probs"], b["topk_idx"], b["topk_w"],
+                    b["expert_counts"])
         mark(1)
         if gather:   # maps only: the gate/up product reads x through row_token
             M.moe_permute(s, b["topk_idx"], None, b["seg_offsets"], b["tile_group"],
                           b["total_rows"], b["row_token"], b["pos"], None, b["ws"])
             mark(2)
             M.grouped_gemm_fwd_gather(s, M.MOE_FWD_GATEUP, X, b["row_token"], b["seg_offsets"],
-                                      b["tile_group"], b["total_rows"], W1, W2, h_save, b["a"],
+                                      b["tile_group"], b["total_rows"], W1, W2, None, b["a"],
                                       b["y_perm"])
         else:
             M.moe_permute(s, b["topk_idx"], X, b["seg_offsets"], b["tile_group"],
                           b["total_rows"], b["row_token"], b["pos"], b["x_perm"], b["ws"])
             mark(2)
             M.grouped_gemm_fwd(s, M.MOE_FWD_GATEUP, b["x_perm"], b["seg_offsets"],
-                               b["tile_group"], b["total_rows"], W1, W2, h_save, b["a"],
+                               b["tile_group"], b["total_rows"], W1, W2, None, b["a"],
                                b["y_perm"])
         mark(3)
         M.grouped_gemm_fwd(s, M.MOE_FWD_DOWN, None, b["seg_offsets"], b["tile_group"],
-                           b["total_rows"], W1, W2, h_save, b["a"], b["y_perm"])
+                           b["total_rows"], W1, W2, None, b["a"], b["y_perm"])
         mark(4)
         M.moe_combine(s, b["y_perm"], b["pos"], b["topk_w"], b["seg_offsets"], b["y"])
         mark(5)
-        if not fwd_bwd:
-            return
+
+    step()
+    torch.cuda.synchronize()
+    counts = b["expert_counts"].cpu().numpy()
+    seg = b["seg_offsets"].cpu().numpy()
+    ms, st_ms = _time_steps(torch, np, step, len(stages), steps, warmup)
+    stage_ms = dict(zip(stages, st_ms))
+    rows = T * K + S * T                        # useful rows
+    padded = int(seg[-1])                      # rows the grouped GEMMs run (segments padded to B)
+    touched = int(np.sum(counts > 0)) + S      # groups whose weights are read
+    per_row = {"fwd_gateup": 4.0 * H * I, "fwd_down": 2.0 * H * I}
+    gemm_flops = sum(per_row.values()) * rows
+    layer_flops = gemm_flops + 2.0 * T * H * E                  # plus the router's fp32 logits
+    out = {"workload": DESC[name], "T": T, "H": H, "E": E, "K": K, "I": I, "S": S, "block_m": B,
+           "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+           "useful_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
+           "frac": round(layer_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+           "stages_tflops": {k: round(per_row[k] * rows / (stage_ms[k] * 1e-3) / 1e12, 1)
+                             for k in per_row},
+           "rows_useful": rows, "rows_padded": padded,
+           "padding_excess": round(padded / rows - 1.0, 4),
+           "experts_touched": touched,
+           "permutation": ("rows of x gathered inside the gate/up GEMM (moe_permute writes the "
+                           "maps only, no x_perm)") if gather else "x_perm written by moe_permute"}
+    if B < 128:
+        # decode: each launch streams the weights of every touched expert once
+        wbytes = {"fwd_gateup": touched * 2 * I * H * 2, "fwd_down": touched * H * I * 2}
+        gbs = {k: wbytes[k] / (stage_ms[k] * 1e-3) / 1e9 for k in wbytes}
+        both = sum(wbytes.values()) / ((stage_ms["fwd_gateup"] + stage_ms["fwd_down"]) * 1e-3) / 1e9
+        out["weight_stream_gbs"] = {k: round(v, 1) for k, v in gbs.items()}
+        out["hbm_frac"] = round(both / PEAK_HBM_GBS, 4)
+        dom = max(wbytes, key=lambda k: stage_ms[k])
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbs[dom], 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(gbs[dom] / PEAK_HBM_GBS, 4),
+                           "traffic": load_traffic(dom, name), "kernel": dom,
+                           "per_unit": f"{wbytes[dom] // touched} weight bytes per touched expert x "
+                                       f"{touched} experts per launch",
+                           "avg_launch_ms": round(stage_ms[dom], 4)}
+    else:
+        dom = max(per_row, key=lambda k: stage_ms[k])
+        ach = per_row[dom] * rows / (stage_ms[dom] * 1e-3) / 1e12
+        traffic = load_traffic(dom, name)
+        out["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                           "traffic": traffic, "kernel": dom,
+                           "per_unit": f"{per_row[dom]:.0f} FLOP per useful row x {rows} rows "
+                                       f"per launch",
+                           "avg_launch_ms": round(stage_ms[dom], 4)}
+    out["clock"] = sample_clock(torch, clock, step)
+    return out, (x, wg, lb, sb, cfg)
+
+
+# ------------------------------------------------------------------------------------------------
+# the training step (forward + backward)
+# ------------------------------------------------------------------------------------------------
+def run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock):
+    cfg = Sy.get_config(name)
+    T, H, E, K, I, S, B = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.S, cfg.block_m
+    dy, logits = Sy.draw_dy(cfg), Sy.uniform_logits(cfg)
+    s = M.make_shape(T, H, E, K, I, S, B)
+    b = M.alloc_buffers(s, dev, backward=True, save_h=True)
+    X = _bf(np, torch, x, dev)
+    DY, LG = _bf(np, torch, dy, dev), torch.from_numpy(logits).to(dev)
+    stages = ["route", "permute", "fwd_gateup", "fwd_down", "combine", "combine_bwd", "dgrad_down",
+              "dgrad_gateup", "wgrad_down", "wgrad_gateup", "unpermute_bwd"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        M.moe_route(s, None, None, None, None, LG, b["probs"], b["topk_idx"], b["topk_w"],
+                    b["expert_counts"])
+        mark(1)
+        M.moe_permute(s, b["topk_idx"], X, b["seg_offsets"], b["tile_group"], b["total_rows"],
+                      b["row_token"], b["pos"], b["x_perm"], b["ws"])
+        mark(2)
+        M.grouped_gemm_fwd(s, M.MOE_FWD_GATEUP, b["x_perm"], b["seg_offsets"], b["tile_group"],
+                           b["total_rows"], W1, W2, b["h_save"], b["a"], b["y_perm"])
+        mark(3)
+        M.grouped_gemm_fwd(s, M.MOE_FWD_DOWN, None, b["seg_offsets"], b["tile_group"],
+                           b["total_rows"], W1, W2, b["h_save"], b["a"], b["y_perm"])
+        mark(4)
+        M.moe_combine(s, b["y_perm"], b["pos"], b["topk_w"], b["seg_offsets"], b["y"])
+        mark(5)
         M.moe_combine_bwd(s, DY, b["y_perm"], b["pos"], b["topk_w"], b["seg_offsets"],
                           b["row_token"], b["total_rows"], b["dy_perm"], b["dtopk_w"])
         for i, which in enumerate((M.MOE_DGRAD_DOWN, M.MOE_DGRAD_GATEUP, M.MOE_WGRAD_DOWN,
@@ -298,97 +449,69 @@ def main():
     step()
     torch.cuda.synchronize()
     counts = b["expert_counts"].cpu().numpy()
-    if fwd_bwd:   # the uniform assignment gives every expert T*K/E rows
-        assert np.all(counts == T * K // E), "uniform routing not reproduced"
+    assert np.all(counts == T * K // E), "uniform routing not reproduced"
     ms_step, st_ms = _time_steps(torch, np, step, len(stages), args.steps, args.warmup)
     stage_ms = dict(zip(stages, st_ms))
-    router_bwd = (router_backward_timing(torch, np, M, Sy, cfg, s, b, X, dev)
-                  if args.workload == "c2" else None)
 
     rows = T * K + S * T                       # useful rows (padding excluded)
-    per_row = {"fwd_gateup": 4.0 * H * I, "fwd_down": 2.0 * H * I}
-    if fwd_bwd:
-        per_row.update({"dgrad_down": 2.0 * H * I, "dgrad_gateup": 4.0 * H * I,
-                        "wgrad_down": 2.0 * H * I, "wgrad_gateup": 4.0 * H * I})
+    per_row = {"fwd_gateup": 4.0 * H * I, "fwd_down": 2.0 * H * I, "dgrad_down": 2.0 * H * I,
+               "dgrad_gateup": 4.0 * H * I, "wgrad_down": 2.0 * H * I, "wgrad_gateup": 4.0 * H * I}
     step_flops = sum(per_row.values()) * rows
     value = step_flops / (ms_step * 1e-3) / 1e12
     dom = max(per_row, key=lambda k: stage_ms[k])
-    touched = int(np.sum(counts > 0)) + S      # groups whose weights are read
-    if args.workload == "c5":
-        # decode: each launch streams the weights of every touched expert once
-        wbytes = {"fwd_gateup": touched * 2 * I * H * 2, "fwd_down": touched * H * I * 2}
-        dom = max(wbytes, key=lambda k: stage_ms[k])
-        gbs = wbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                    "traffic": load_traffic(dom, args.workload), "kernel": dom,
-                    "per_unit": f"{wbytes[dom] // touched} weight bytes per touched expert x "
-                                f"{touched} experts per launch",
-                    "avg_launch_ms": round(stage_ms[dom], 4)}
-    else:
-        dom_flops = per_row[dom] * rows
-        achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
-        traffic = load_traffic(dom, args.workload)
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic, "kernel": dom,
-                    "traffic_gbs": (round(traffic / (stage_ms[dom] * 1e-3) / 1e9, 1)
-                                    if traffic is not None else None),
-                    "per_unit": f"{per_row[dom]:.0f} FLOP per useful row x {rows} rows per launch",
-                    "avg_launch_ms": round(stage_ms[dom], 4)}
-    desc = {"dense": "dense SwiGLU FFN as one group, forward+backward (T=8192, hidden=4096, "
-                     "intermediate=11264, block_m=128)",
-            "c2": "grouped-GEMM MoE FFN forward+backward, uniform routing (T=8192, hidden=4096, "
-                  "128 experts top-6, intermediate=1408, block_m=128, 384 rows per expert)",
-            "ep8": "one GPU's share of the 128-expert layer under 8-way expert parallelism, "
-                   "forward+backward: 16 experts x 3072 rows (T=8192 top-6 uniform over 16 "
-                   "experts, hidden=4096, intermediate=1408, block_m=128)",
-            "c3": "MoE FFN full layer forward from x, skewed routing (T=16384, hidden=4096, 128 "
-                  "experts top-6 with Zipf(1.1) logit offsets + 2 shared experts, intermediate=1408, "
-                  "block_m=128)",
-            "c5": "MoE FFN decode forward from x, random routing (T=256, hidden=4096, 128 experts "
-                  "top-6 + 2 shared experts, intermediate=1408, block_m=16)"}[args.workload]
+    dom_flops = per_row[dom] * rows
+    achieved = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
+    traffic = load_traffic(dom, name)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": dom,
+                "traffic_gbs": (round(traffic / (stage_ms[dom] * 1e-3) / 1e9, 1)
+                                if traffic is not None else None),
+                "per_unit": f"{per_row[dom]:.0f} FLOP per useful row x {rows} rows per launch",
+                "avg_launch_ms": round(stage_ms[dom], 4)}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": desc, "T": T, "H": H, "E": E, "K": K, "I": I, "S": S, "block_m": B},
+        "config": {"workload": DESC[name], "T": T, "H": H, "E": E, "K": K, "I": I, "S": S,
+                   "block_m": B},
         "roofline": roofline,
-        "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "training_step_tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
         "step_useful_tflop": round(step_flops / 1e12, 4),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stages_tflops": {k: round(per_row[k] * rows / (stage_ms[k] * 1e-3) / 1e12, 1)
                           for k in per_row},
-        "experts_touched": touched,
-        "permutation": ("rows of x gathered inside the gate/up GEMM (moe_permute writes the maps "
-                        "only, no x_perm)") if gather else "x_perm written by moe_permute",
+        "experts_touched": int(np.sum(counts > 0)) + S,
+        "permutation": "x_perm written by moe_permute",
     }
     # The forward, data-gradient and weight-gradient passes, each its two grouped GEMMs.
-    passes = {"fwd": ("fwd_gateup", "fwd_down"), "dx": ("dgrad_down", "dgrad_gateup"),
-              "dw": ("wgrad_down", "wgrad_gateup")}
     out["passes"] = {}
-    for name, ks in passes.items():
-        if not all(k in per_row for k in ks):
-            continue
+    for pname, ks in (("fwd", ("fwd_gateup", "fwd_down")), ("dx", ("dgrad_down", "dgrad_gateup")),
+                      ("dw", ("wgrad_down", "wgrad_gateup"))):
         t = sum(stage_ms[k] for k in ks)
         tf = sum(per_row[k] for k in ks) * rows / (t * 1e-3) / 1e12
-        out["passes"][name] = {"ms": round(t, 4), "tflops": round(tf, 1),
-                               "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
-    if router_bwd is not None:
-        out["router_backward"] = router_bwd
-    if args.workload == "c2":
+        out["passes"][pname] = {"ms": round(t, 4), "tflops": round(tf, 1),
+                                "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    out["clock"] = sample_clock(torch, clock, step)
+    if out["clock"]:
+        c = out["clock"]["median_mhz"]
+        # the same fractions against the dense bf16 peak at the sampled clock
+        out["passes_frac_at_sampled_clock"] = {
+            k: round(v["frac"] * NOMINAL_CLOCK_MHZ / c, 4) for k, v in out["passes"].items()}
+    if name == "c2":
+        out["router_backward"] = router_backward_timing(torch, np, M, Sy, cfg, s, b, X, dev)
         # The fp32-gradient variant of the two weight-gradient GEMMs on the step's own operands.
         dw1f = torch.empty(E, 2 * I, H, device=dev)
         dw2f = torch.empty(E, H, I, device=dev)
         wg32 = {}
-        for name, which in (("wgrad_down", M.MOE_WGRAD_DOWN), ("wgrad_gateup", M.MOE_WGRAD_GATEUP)):
+        for wname, which in (("wgrad_down", M.MOE_WGRAD_DOWN), ("wgrad_gateup", M.MOE_WGRAD_GATEUP)):
             t = _time_call(torch, np, lambda: M.grouped_gemm_wgrad_f32(
                 s, which, b["x_perm"], b["a"], b["dy_perm"], b["dh"], b["seg_offsets"], dw1f, dw2f),
                 10)
-            wg32[name] = {"ms": round(t, 4),
-                          "tflops": round(per_row[name] * rows / (t * 1e-3) / 1e12, 1)}
+            wg32[wname] = {"ms": round(t, 4),
+                           "tflops": round(per_row[wname] * rows / (t * 1e-3) / 1e12, 1)}
         out["wgrad_fp32_dw"] = wg32
         del dw1f, dw2f
         # Context only: the gate/up product as a plain batched library GEMM (torch.bmm, served by
@@ -402,7 +525,7 @@ def main():
             "ms": round(t_lib, 4), "tflops": round(4.0 * T * K * H * I / (t_lib * 1e-3) / 1e12, 1),
             "this_library_fwd_gateup_ms": round(stage_ms["fwd_gateup"], 4)}
         del W1t
-    if args.workload == "dense":
+    if name == "dense":
         # Context only: the same gate/up product as one plain library GEMM (torch.mm, which ROCm
         # serves with hipBLASLt), on the same operands, outside the step.
         W1t = W1.view(2 * I, H).t().contiguous()
@@ -412,12 +535,110 @@ def main():
             "ms": round(t_lib, 4), "tflops": round(4.0 * T * H * I / (t_lib * 1e-3) / 1e12, 1),
             "this_library_fwd_gateup_ms": round(stage_ms["fwd_gateup"], 4)}
         del W1t
-    sample = args.cpu_sample if args.cpu_sample is not None else {"c2": 384, "c3": 256, "dense": 8192,
-                                                                   "c5": 256, "ep8": 384}[args.workload]
-    if sample > 0:
-        log(f"[bench] CPU oracle on {sample} tokens")
-        out["cpu_baseline"] = (cpu_baseline_fwd_bwd(cfg, x, w1, w2, logits, dy, sample) if fwd_bwd
-                               else cpu_baseline_fwd(cfg, x, w1, w2, wg, lb, sb, sample))
+    del b
+    return out, (dy, logits)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=("c2", "c3", "c5", "dense", "ep8"), default="c2",
+                    help="c2: forward+backward at the uniform 8192-token shape (default; the line "
+                         "also carries the c3 and c5 forwards); c3: skewed 16384-token full layer "
+                         "forward; c5: 256-token decode forward; dense: forward+backward of a dense "
+                         "SwiGLU FFN (intermediate 11264) as one group; ep8: forward+backward of one "
+                         "GPU's 16-expert share under 8-way expert parallelism (3072 rows per expert)")
+    ap.add_argument("--no-forwards", action="store_true",
+                    help="c2: leave out the c3 and c5 forward sub-objects")
+    ap.add_argument("--forward-steps", type=int, default=10,
+                    help="timed steps of each c3/c5 forward sub-object")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before warmup, copy a cold buffer of this many MiB (a plain copy of known "
+                         "size that scales the HBM byte counters)")
+    ap.add_argument("--materialize", action="store_true",
+                    help="c3/c5: write x_perm in moe_permute and run grouped_gemm_fwd on it instead "
+                         "of gathering x's rows inside the gate/up product")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="CPU oracle sample (0 = skip the CPU baseline): for the training workloads "
+                         "the token stride (default 8: 1024 tokens, 48 experts x 128 rows, no "
+                         "padding), for c3/c5 the number of leading tokens (default 256)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): the library "
+              f"implements the single-GPU path only; sharding the experts across GPUs (an "
+              f"all-to-all of the permuted rows each way) is not implemented.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import grouped_gemm_fp32_amd as M
+    import synth as Sy
+
+    dev = "cuda:0"
+    clock = ClockSampler()
+    name = args.workload
+    cfg = Sy.get_config(name)
+    log(f"[bench] {name}: generating inputs {cfg}")
+    t0 = time.perf_counter()
+    extras = name == "c2" and not args.no_forwards
+    if name in ("c2", "c3"):
+        # c3's 130 groups share their first 128 with c2 (the same per-group streams, seed 0)
+        w_cfg = Sy.get_config("c3") if (name == "c3" or extras) else cfg
+    else:
+        w_cfg = cfg
+    w1, w2 = Sy.draw_w1_all(w_cfg), Sy.draw_w2_all(w_cfg)
+    log(f"[bench] weights ready in {time.perf_counter() - t0:.1f}s; uploading")
+    W1a, W2a = _bf(np, torch, w1, dev), _bf(np, torch, w2, dev)
+    G = cfg.E + cfg.S
+    W1, W2 = W1a[:G], W2a[:G]
+    torch.cuda.synchronize()
+
+    if name in ("c3", "c5"):
+        fwd, (x, wg, lb, sb, _) = run_forward(torch, np, M, Sy, name, W1, W2, dev, args.steps,
+                                              args.warmup, args.materialize, clock)
+        rows, T = fwd["rows_useful"], cfg.T
+        out = {"metric": METRIC, "value": fwd["useful_tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": fwd["ms"],
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "data": "synthetic",
+               "config": {"workload": DESC[name], "T": T, "H": cfg.H, "E": cfg.E, "K": cfg.K,
+                          "I": cfg.I, "S": cfg.S, "block_m": cfg.block_m},
+               "roofline": fwd.pop("roofline"), "tokens_per_s": fwd["tokens_per_s"],
+               "mfma_frac": fwd["frac"]}
+        out.update({k: v for k, v in fwd.items() if k not in out})
+        sample = args.cpu_sample if args.cpu_sample is not None else 256
+        if sample > 0:
+            log(f"[bench] CPU oracle on {sample} tokens")
+            out["cpu_baseline"] = cpu_baseline_fwd(cfg, x, w1[:G], w2[:G], wg, lb, sb, sample)
+        else:
+            out["cpu_baseline"] = None
+        print(json.dumps(out), flush=True)
+        return
+
+    x = Sy.draw_x(cfg)
+    out, (dy, logits) = run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock)
+    if extras:
+        log("[bench] c3 forward (skewed full layer)")
+        out["layer_c3"], _ = run_forward(torch, np, M, Sy, "c3", W1a, W2a, dev, args.forward_steps,
+                                         3, args.materialize, clock)
+        log("[bench] c5 forward (decode): drawing its weights")
+        del W1a, W2a, W1, W2
+        torch.cuda.empty_cache()
+        c5 = Sy.get_config("c5")
+        W15 = _bf(np, torch, Sy.draw_w1_all(c5), dev)
+        W25 = _bf(np, torch, Sy.draw_w2_all(c5), dev)
+        out["decode_c5"], _ = run_forward(torch, np, M, Sy, "c5", W15, W25, dev,
+                                          max(args.forward_steps, 20), 5, args.materialize, clock)
+        del W15, W25
+    stride = args.cpu_sample if args.cpu_sample is not None else 8
+    if stride > 0:
+        log(f"[bench] CPU oracle on one token in {stride}")
+        G = cfg.E + cfg.S
+        out["cpu_baseline"] = cpu_baseline_fwd_bwd(cfg, x, w1[:G], w2[:G], logits, dy, stride)
+        out["cpu_baseline"]["gpu_over_cpu"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void gather_sum_kernel(int H, int E, int 
     float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-      if (j < K) {
+      if (j < K && rows[j] >= 0) {   // pos < 0: a slot that got no row (invalid expert index)
         const uint4 v = reinterpret_cast<const uint4*>(src + rows[j] * H)[c];
         if (WEIGHTED) acc8(a, v, wt[j]); else add8(a, v);
       }
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(int H, int E, int
                          lo_bf(g.z), hi_bf(g.z), lo_bf(g.w), hi_bf(g.w)};
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-      if (j < K) {
+      if (j < K && rows[j] >= 0) {   // pos < 0: no row (invalid expert index); dtopk_w = 0
         const uint4 v = reinterpret_cast<const uint4*>(y_perm + rows[j] * H)[c];
         float d = 0.0f;
         d += gv[0] * lo_bf(v.x); d += gv[1] * hi_bf(v.x);

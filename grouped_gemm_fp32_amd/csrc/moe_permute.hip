@@ -118,12 +118,13 @@ __global__ __launch_bounds__(kSegThreads) void perm_segment_kernel(
     }
     tile_group[i] = g;
   }
-  // Padding rows of every segment.
+  // Every row of every segment starts as padding (-1); the scatter then writes the token of each
+  // routed and shared row. With valid routing that leaves -1 exactly on the padding rows; with
+  // out-of-range or repeated expert indices (which the contract excludes) a row no slot claims
+  // stays -1 instead of holding whatever the buffer held.
   const int lane = tid & 63, wave = tid >> 6;
-  for (int g = wave; g < G; g += kSegThreads / 64) {
-    const int c = g < E ? cnt[g] : T;
-    for (int r = seg[g] + c + lane; r < seg[g + 1]; r += 64) row_token[r] = -1;
-  }
+  for (int g = wave; g < G; g += kSegThreads / 64)
+    for (int r = seg[g] + lane; r < seg[g + 1]; r += 64) row_token[r] = -1;
 }
 
 __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
@@ -162,7 +163,10 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
     const int tl = t - t0;
     for (int j = 0; j < K; ++j) {
       const int e = idx[(int64_t)t * K + j];
-      if (e < 0 || e >= E) continue;
+      if (e < 0 || e >= E) {   // out of range (excluded by the contract): no row, pos = -1
+        pos[(int64_t)t * K + j] = -1;
+        continue;
+      }
       const int w = tl >> 5;
       const int rank = pref[e * W + w] + __popc(mask[e * W + w] & ((1u << (tl & 31)) - 1u));
       const int r = segs[e] + rank;
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
 // One wavefront per row: x_perm[r] = x[row_token[r]] (or 0), 16 B per lane per step.
 constexpr int kGatherU = 8;   // 16-byte chunks per lane per batch (a 4096-wide row in one batch)
 
-__global__ __launch_bounds__(kThreads) void gather_rows_kernel(int H, int64_t mcap,
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(int T, int H, int64_t mcap,
                                                                const int32_t* __restrict__ total,
                                                                const int32_t* __restrict__ row_token,
                                                                const uint16_t* __restrict__ x,
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(int H, int64_t mc
   const int t = row_token[r];
   const int nv = H / 8;
   uint4* dst = reinterpret_cast<uint4*>(x_perm + r * H);
-  if (t < 0) {
+  if (t < 0 || t >= T) {   // padding (a token index past T never comes from the scatter)
     for (int c = lane; c < nv; c += 64) dst[c] = make_uint4(0, 0, 0, 0);
   } else {
     // all of a batch's loads are issued before its stores, so a wavefront keeps kGatherU 16-byte
@@ -240,7 +244,7 @@ hipError_t launch_permute(const moe_shape_t& s, int64_t mcap, const int32_t* top
   if (x) {
     const int64_t rows_per_wg = kThreads / 64;
     hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((mcap + rows_per_wg - 1) / rows_per_wg)),
-                       dim3(kThreads), 0, st, s.H, mcap, total_rows, row_token, x, x_perm);
+                       dim3(kThreads), 0, st, s.T, s.H, mcap, total_rows, row_token, x, x_perm);
   }
   return hipGetLastError();
 }

@@ -130,7 +130,10 @@ moe_status_t moe_route(const moe_shape_t* shape, const uint16_t* x, const float*
  *   pos[T,K]:         row of token t's slot j in its expert's segment.
  *   x_perm[Mcap,H]:   x[row_token[r]] or 0 on padding rows, r < total_rows (skipped if x == NULL;
  *                     with x given, x and x_perm must be 16-byte aligned).
- * topk_idx entries must lie in [0, E) and be distinct per token (moe_route guarantees it).
+ * topk_idx entries must lie in [0, E) and be distinct per token (moe_route guarantees it). Other
+ * indices give unspecified outputs but no access out of bounds: an entry outside [0, E) gets
+ * pos = -1, which moe_combine, moe_combine_bwd and moe_unpermute_bwd skip, and a segment row that
+ * no slot claims (a repeated expert) has row_token = -1 and reads as padding.
  * ws: device scratch of at least moe_workspace_size(shape) bytes (unused when T == 0).
  */
 moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_idx, const uint16_t* x,

@@ -42,3 +42,22 @@ def test_cpu_baseline_record():
     rec = bench.cpu_baseline_fwd(cfg, x, w1, w2, Sy.draw_wg(cfg), None, Sy.draw_sel_bias(cfg), 16)
     assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
     assert rec["value"] > 0 and rec["cores"] >= 1 and "16 tokens" in rec["sample"]
+
+
+def test_training_cpu_baseline_sample_has_no_padding():
+    """One token in 32 of the uniformly routed 8192-token batch goes to 12 experts with exactly
+    128 rows each (one whole block), so the timed oracle sample computes no padding rows."""
+    import synth as Sy
+    cfg = Sy.get_config("c2", H=128, I=64)
+    x, w1, w2 = Sy.draw_x(cfg), Sy.draw_w1_all(cfg), Sy.draw_w2_all(cfg)
+    rec = bench.cpu_baseline_fwd_bwd(cfg, x, w1, w2, Sy.uniform_logits(cfg), Sy.draw_dy(cfg), 32)
+    assert rec["rows_useful"] == 256 * 6 and rec["rows_padded"] == rec["rows_useful"]
+    assert rec["padded_over_useful"] == 1.0 and rec["cpu_model"]
+    assert "one token in 32" in rec["sample"]
+
+
+def test_clock_sampler_without_a_gpu_reports_nothing():
+    c = bench.ClockSampler()
+    with c:
+        pass
+    assert c.summary() is None or c.summary()["samples"] >= 1
