@@ -477,6 +477,14 @@ constexpr uint32_t kPastEnd = 0x80000000u;
 // M0 is a reserved register, so the compiler would not honour it in a clobber list: the block
 // saves and restores it. On GFX9-family hardware an LDS DMA that reads M0 right after a scalar
 // write of M0 needs one wait state in between, hence the s_nop.
+// The same with the non-temporal hint, for operands read exactly once (the expert weights): L2
+// then keeps the activation panels that the tiles of a segment share.
+__device__ __forceinline__ void dma16_nt(v4u32_t r, uint32_t voff, uint32_t lds_wave) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+               "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(uniform(lds_wave)), "v"(voff), "s"(r) : "memory");
+}
 __device__ __forceinline__ void dma16(v4u32_t r, uint32_t voff, uint32_t lds_wave) {
   uint32_t saved;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
@@ -978,6 +986,29 @@ struct Eng8 {
   lds_u8_t* s3;
   uint32_t lds_base;
   int lane, wave, wm, wn;
+  // false when this wavefront's output columns of the current tile all lie at or past N (the
+  // ragged last column tile, e.g. N = 1408 = 5.5 x 256): it then still issues its share of the
+  // DMA and meets every barrier, but reads no fragments and issues no MFMAs.
+  // Only the down projection's gradients have N = I, which need not be a multiple of 256 (1408 is
+  // 5.5 tiles); elsewhere the check is compiled out, leaving the hot loop as it was.
+  static constexpr bool kRagged = KIND == kDgradDown || KIND == kWgradDown;
+  bool mma_on = true;
+  // Per tile: where the upper column half lies wholly at or past N, waves w and w + 4 (which share
+  // a SIMD) take the same row band and the two halves, so each SIMD keeps one busy wavefront;
+  // elsewhere waves 2r and 2r + 1 take row band r (measured faster on whole tiles).
+  __device__ __forceinline__ void set_tile_cols(int n0) {
+    if constexpr (!kRagged) return;
+    constexpr bool split = KindTraits<KIND>::split;
+    const int n_lim = split ? p.I : p.N, half = split ? TL::WTN / 2 : TL::WTN;
+    if (n0 + half >= n_lim) {
+      wm = wave % TL::WM;
+      wn = wave / TL::WM;
+    } else {
+      wm = wave / TL::WN;
+      wn = wave % TL::WN;
+    }
+    mma_on = n0 + wn * half < n_lim;
+  }
   // DMA state of one tile: buffer resources and one lane offset per operand; instruction i adds
   // a wave-uniform stride, stage kt adds kt * kstep.
   struct Dma {
@@ -992,6 +1023,7 @@ struct Eng8 {
     lds_base = (uint32_t)(uintptr_t)s3;
     lane = threadIdx.x & 63;
     wave = (int)uniform((uint32_t)(threadIdx.x >> 6));
+    static_assert(TL::WN == 2 && TL::NW == 8, "two column halves over eight wavefronts");
     wm = wave / TL::WN;
     wn = wave % TL::WN;
     a_kstep = AMN ? (uint32_t)(BK * p.lda * 2) : (uint32_t)(BK * 2);
@@ -1056,8 +1088,12 @@ struct Eng8 {
   __device__ __forceinline__ void dma_one(const Dma& st, int d, int kt, int slot) const {
     const uint32_t sl = lds_base + slot * STAGE;
     if (d < LB) {
-      dma16(st.rb, st.b_off0 + uniform(kt * b_kstep + b_istride(d)),
-            sl + A_BYTES + (d * NW + wave) * 1024);
+      if constexpr (Tr::grouped_rows)   // the expert weights: read once per launch
+        dma16_nt(st.rb, st.b_off0 + uniform(kt * b_kstep + b_istride(d)),
+                 sl + A_BYTES + (d * NW + wave) * 1024);
+      else
+        dma16(st.rb, st.b_off0 + uniform(kt * b_kstep + b_istride(d)),
+              sl + A_BYTES + (d * NW + wave) * 1024);
     } else {
       const int i = d - LB;
       if constexpr (GA) dma16(st.ra, st.a_offs[i] + uniform(kt * a_kstep), sl + (i * NW + wave) * 1024);
@@ -1097,6 +1133,7 @@ struct Eng8 {
     return r;
   }
   __device__ __forceinline__ void load(int slot, int kk, Frags& f) const {
+    if (kRagged && !mma_on) return;
     const int sa = slot * STAGE, sb = sa + A_BYTES;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -1116,6 +1153,14 @@ struct Eng8 {
   __device__ __forceinline__ void mma_dma(Acc& acc, const Frags& f, bool on, const Dma& st,
                                           int kt_dma, int slot_dma, int nd = D1 - D0) const {
     constexpr int N = D1 - D0, T = TM * TN;
+    if (kRagged && !mma_on) {   // nothing to compute in this tile: only this wave's DMA share
+      if constexpr (N > 0) {
+#pragma unroll
+        for (int d = 0; d < N; ++d)
+          if (on && d < nd) dma_one(st, D0 + d, kt_dma, slot_dma);
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       acc[t / TN][t % TN] = Mf::run(f.b[t % TN], f.a[t / TN], acc[t / TN][t % TN]);
@@ -1197,6 +1242,7 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
                                            int n0, int kbeg, int klen) {
   typedef Eng8<KIND, TL, GA> E;
   E e(p, smem);
+  e.set_tile_cols(n0);
   typename E::Dma st;
   e.setup(st, g, m0, n0, kbeg, klen);
   typename E::Acc acc;
@@ -1217,6 +1263,7 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
   static_assert(2 * TL::STAGE / TL::NW >= 8192, "8 KiB of LDS per wavefront for the epilogue");
   wait_lgkm0();
   block_barrier();
+  if (E::kRagged && !e.mma_on) return;   // every column of this wave is at or past N
   store_tile8<KIND, TL::TM, TL::TN, TL::WTM, TL::WTN>(p, acc, g, m0, n0, e.wm, e.wn, e.lane,
                                                       smem + e.wave * (2 * TL::STAGE / TL::NW));
 }
@@ -1420,6 +1467,7 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) 
     }
     typename E::Acc acc;
     E::zero(acc);
+    e.set_tile_cols(cur.n0);
     const int64_t ln = l + nwg;
     const bool has_next = ln < lend;
     T nxt = cur;
