@@ -403,6 +403,14 @@ def run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock):
     DY, LG = _bf(np, torch, dy, dev), torch.from_numpy(logits).to(dev)
     stages = ["route", "permute", "fwd_gateup", "fwd_down", "combine", "combine_bwd", "dgrad_down",
               "dgrad_gateup", "wgrad_down", "wgrad_gateup", "unpermute_bwd"]
+    # The unpermute backward needs only dx_perm, so it runs on a second stream beside the two
+    # weight-gradient GEMMs (it takes little LDS and few registers, so its workgroups fit on the
+    # CUs beside theirs); the step ends when both streams are done. Its own events are on that
+    # stream.
+    side = torch.cuda.Stream() if not args.serial else None
+    side_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(args.steps)]
+    side_k = [0]
 
     def step(ev=None):
         def mark(i):
@@ -428,11 +436,28 @@ def run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock):
         for i, which in enumerate((M.MOE_DGRAD_DOWN, M.MOE_DGRAD_GATEUP, M.MOE_WGRAD_DOWN,
                                    M.MOE_WGRAD_GATEUP)):
             mark(6 + i)
+            if side is not None and which == M.MOE_WGRAD_DOWN:
+                done = torch.cuda.Event()
+                done.record()
+                side.wait_event(done)
+                with torch.cuda.stream(side):
+                    if ev is not None:
+                        side_ev[side_k[0]][0].record()
+                    M.moe_unpermute_bwd(s, b["dx_perm"], b["pos"], b["seg_offsets"], b["dx"])
+                    if ev is not None:
+                        side_ev[side_k[0]][1].record()
             M.grouped_gemm_bwd(s, which, b["x_perm"], b["h_save"], b["a"], b["dy_perm"],
                                b["seg_offsets"], b["tile_group"], b["total_rows"], W1, W2, b["dh"],
                                b["dx_perm"], b["dw1"], b["dw2"])
         mark(10)
-        M.moe_unpermute_bwd(s, b["dx_perm"], b["pos"], b["seg_offsets"], b["dx"])
+        if side is None:
+            M.moe_unpermute_bwd(s, b["dx_perm"], b["pos"], b["seg_offsets"], b["dx"])
+        else:
+            joined = torch.cuda.Event()
+            joined.record(side)
+            torch.cuda.current_stream().wait_event(joined)
+            if ev is not None:
+                side_k[0] += 1
         mark(11)
 
     if args.calib_copy_mib > 0:
@@ -452,6 +477,8 @@ def run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock):
     assert np.all(counts == T * K // E), "uniform routing not reproduced"
     ms_step, st_ms = _time_steps(torch, np, step, len(stages), args.steps, args.warmup)
     stage_ms = dict(zip(stages, st_ms))
+    if side is not None:   # on its own stream, beside the weight-gradient GEMMs
+        stage_ms["unpermute_bwd"] = float(np.mean([e[0].elapsed_time(e[1]) for e in side_ev]))
 
     rows = T * K + S * T                       # useful rows (padding excluded)
     per_row = {"fwd_gateup": 4.0 * H * I, "fwd_down": 2.0 * H * I, "dgrad_down": 2.0 * H * I,
@@ -485,6 +512,8 @@ def run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock):
                           for k in per_row},
         "experts_touched": int(np.sum(counts > 0)) + S,
         "permutation": "x_perm written by moe_permute",
+        "streams": ("the unpermute backward on a second stream beside the weight-gradient GEMMs"
+                    if side is not None else "one stream"),
     }
     # The forward, data-gradient and weight-gradient passes, each its two grouped GEMMs.
     out["passes"] = {}
@@ -550,6 +579,9 @@ def main():
                          "forward; c5: 256-token decode forward; dense: forward+backward of a dense "
                          "SwiGLU FFN (intermediate 11264) as one group; ep8: forward+backward of one "
                          "GPU's 16-expert share under 8-way expert parallelism (3072 rows per expert)")
+    ap.add_argument("--serial", action="store_true",
+                    help="training step: run the unpermute backward after the weight gradients on "
+                         "the one stream instead of beside them on a second stream")
     ap.add_argument("--no-forwards", action="store_true",
                     help="c2: leave out the c3 and c5 forward sub-objects")
     ap.add_argument("--forward-steps", type=int, default=10,
