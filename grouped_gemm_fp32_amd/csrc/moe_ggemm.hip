@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "moe_common.h"
+#include "moe_dma.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -449,73 +450,7 @@ __global__ __launch_bounds__(kThreads, 2) void ggemm_kernel(GemmArgs p) {
 // the stage STAGES ahead. STAGES - 1 stages are in flight while a stage is computed.
 // ------------------------------------------------------------------------------------------------
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef uint32_t v4u32_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
-
-// Buffer resource (gfx9 layout): 48-bit base, stride 0, num_records = bytes, raw dword format.
-__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ v4u32_t make_rsrc(const void* base, int64_t bytes) {
-  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  v4u32_t r;
-  r.x = uniform((uint32_t)a);
-  r.y = uniform((uint32_t)(a >> 32) & 0xffffu);
-  r.z = uniform(n);
-  r.w = 0x00020000u;
-  return r;
-}
-
-// A lane offset past the end of every buffer resource the gathering kernels build (their sources
-// hold at most 2^31 bytes, which the host checks): the DMA then deposits zeros.
-constexpr uint32_t kPastEnd = 0x80000000u;
-
-// Bounds-checked DMA of 16 bytes per lane from a buffer resource into LDS at lds_wave + 16 * lane.
-// Issued from asm: the instruction has no register result (it writes LDS through M0), and hiding
-// it from the compiler keeps it from draining every DMA before unrelated LDS reads; the kernel's
-// own vmcnt waits and barriers order the data.
-// M0 is a reserved register, so the compiler would not honour it in a clobber list: the block
-// saves and restores it. On GFX9-family hardware an LDS DMA that reads M0 right after a scalar
-// write of M0 needs one wait state in between, hence the s_nop.
-// The same with the non-temporal hint, for operands read exactly once (the expert weights): L2
-// then keeps the activation panels that the tiles of a segment share.
-__device__ __forceinline__ void dma16_nt(v4u32_t r, uint32_t voff, uint32_t lds_wave) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-               "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(uniform(lds_wave)), "v"(voff), "s"(r) : "memory");
-}
-__device__ __forceinline__ void dma16(v4u32_t r, uint32_t voff, uint32_t lds_wave) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-               "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(uniform(lds_wave)), "v"(voff), "s"(r) : "memory");
-}
-
-// Waits, each also a compiler memory barrier so that no LDS access moves across them.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// Wait until at most `later` of this wave's DMA stages (PER instructions each) are in flight.
-template <int PER, int MAXL>
-__device__ __forceinline__ void wait_stages(int later) {
-  if constexpr (MAXL >= 3) {
-    if (later >= 3) { wait_vm<3 * PER>(); return; }
-  }
-  if constexpr (MAXL >= 2) {
-    if (later == 2) { wait_vm<2 * PER>(); return; }
-  }
-  if constexpr (MAXL >= 1) {
-    if (later == 1) { wait_vm<PER>(); return; }
-  }
-  wait_vm<0>();
-}
-
 constexpr int kLdsBytes = 163840;   // gfx950: 160 KiB of LDS per workgroup
 constexpr int kTallBlk = 128;       // row granularity of tall tiles (block_m % 128 == 0)
 constexpr int kTallMaxBlk = 3;      // tallest tile: 3 blocks = 384 rows
@@ -1017,6 +952,11 @@ struct Eng8 {
     uint32_t a_offs[GA ? TL::LA : 1];   // gathered A: one lane offset per DMA instruction
   };
   uint32_t a_kstep, b_kstep;
+  // HD: only waves 0-3 (one per SIMD) issue the DMA, each its own instructions and those of the
+  // wave 4 above it (rows 32 further on, LDS 4 KiB further on), so the other wave of each SIMD
+  // never waits at a full texture queue.
+  static constexpr bool HD = Tr::grouped_rows && !GA;
+  uint32_t a_vs, b_vs;
 
   __device__ __forceinline__ Eng8(const GemmArgs& p_, unsigned char* smem_) : p(p_), smem(smem_) {
     s3 = (lds_u8_t*)smem;
@@ -1028,6 +968,8 @@ struct Eng8 {
     wn = wave % TL::WN;
     a_kstep = AMN ? (uint32_t)(BK * p.lda * 2) : (uint32_t)(BK * 2);
     b_kstep = BMN ? (uint32_t)(BK * p.ldb * 2) : (uint32_t)(BK * 2);
+    a_vs = (uint32_t)(4 * RPI * p.lda * 2);
+    b_vs = BMN ? (uint32_t)((4 * 64 / (BN / 8)) * p.ldb * 2) : (uint32_t)(4 * RPI * p.ldb * 2);
   }
 
   // Tile: rows m0.. of group g (row-grouped kinds) or weight rows m0.. of group g (wgrad),
@@ -1085,11 +1027,11 @@ struct Eng8 {
   // L2 and need the longest head start; the A panel is shared by a segment's column tiles and
   // mostly hits L2.
   static constexpr int LB = TL::LB;
-  __device__ __forceinline__ void dma_one(const Dma& st, int d, int kt, int slot) const {
-    const uint32_t sl = lds_base + slot * STAGE;
+  __device__ __forceinline__ void dma_one(const Dma& st, int d, int kt, int slot, int hv = 0) const {
+    const uint32_t sl = lds_base + slot * STAGE + hv * 4096;
     if (d < LB) {
       if constexpr (Tr::grouped_rows)   // the expert weights: read once per launch
-        dma16_nt(st.rb, st.b_off0 + uniform(kt * b_kstep + b_istride(d)),
+        dma16_nt(st.rb, st.b_off0 + uniform(kt * b_kstep + b_istride(d) + hv * b_vs),
                  sl + A_BYTES + (d * NW + wave) * 1024);
       else
         dma16(st.rb, st.b_off0 + uniform(kt * b_kstep + b_istride(d)),
@@ -1097,10 +1039,20 @@ struct Eng8 {
     } else {
       const int i = d - LB;
       if constexpr (GA) dma16(st.ra, st.a_offs[i] + uniform(kt * a_kstep), sl + (i * NW + wave) * 1024);
-      else dma16(st.ra, st.a_off0 + uniform(kt * a_kstep + a_istride(i)), sl + (i * NW + wave) * 1024);
+      else dma16(st.ra, st.a_off0 + uniform(kt * a_kstep + a_istride(i) + hv * a_vs), sl + (i * NW + wave) * 1024);
     }
   }
   __device__ __forceinline__ void issue_stage(const Dma& st, int kt, int slot) const {
+    if constexpr (HD) {
+      if (wave < 4) {
+#pragma unroll
+        for (int d = 0; d < L; ++d) {
+          dma_one(st, d, kt, slot, 0);
+          dma_one(st, d, kt, slot, 1);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int d = 0; d < L; ++d) dma_one(st, d, kt, slot);
   }
@@ -1157,14 +1109,32 @@ struct Eng8 {
       if constexpr (N > 0) {
 #pragma unroll
         for (int d = 0; d < N; ++d)
-          if (on && d < nd) dma_one(st, D0 + d, kt_dma, slot_dma);
+          if (on && d < nd) {
+            if constexpr (HD) {
+              if (wave < 4) {
+                dma_one(st, D0 + d, kt_dma, slot_dma, 0);
+                dma_one(st, D0 + d, kt_dma, slot_dma, 1);
+              }
+            } else {
+              dma_one(st, D0 + d, kt_dma, slot_dma);
+            }
+          }
       }
       return;
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       acc[t / TN][t % TN] = Mf::run(f.b[t % TN], f.a[t / TN], acc[t / TN][t % TN]);
-      if constexpr (N > 0) {
+      if constexpr (N > 0 && HD) {
+        constexpr int N2 = 2 * N;
+#pragma unroll
+        for (int e2 = 0; e2 < N2; ++e2)
+          if (t == e2 * T / N2 && on && e2 / 2 < nd && wave < 4) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_one(st, D0 + e2 / 2, kt_dma, slot_dma, e2 & 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      } else if constexpr (N > 0) {
 #pragma unroll
         for (int d = 0; d < N; ++d)
           if (t == d * T / N && on && d < nd) {   // d*T/N is in [0, T) for any N
@@ -1252,7 +1222,11 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
     e.issue_stage(st, 0, 0);
     if (nk > 1) {
       e.issue_stage(st, 1, 1);
-      wait_vm<TL::L>();
+      if constexpr (E::HD) {
+        if (e.wave < 4) wait_vm<2 * TL::L>();
+      } else {
+        wait_vm<TL::L>();
+      }
     } else {
       wait_vm<0>();
     }
