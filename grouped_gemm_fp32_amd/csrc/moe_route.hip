@@ -16,6 +16,7 @@
 //      weights, per-expert counts (an LDS histogram per workgroup, then one atomic per expert).
 //      The cross-lane reductions use DPP and permlane swaps, not the LDS crossbar.
 #include "moe_common.h"
+#include "moe_dma.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -121,6 +122,135 @@ __global__ __launch_bounds__(NW * 64) void router_logits_kernel(
       logits[(int64_t)(t0 + tl) * E + e0 + el] = z;
     }
   }
+}
+
+// 16-byte chunk position of chunk c in a 128-byte K-major LDS row r (an involution): the 16 rows
+// a 16-lane group reads land on distinct bank slots.
+__device__ __forceinline__ int kswz64(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// ---- 1b. router logits for large batches, operands staged in LDS ---------------------------------
+// 64 tokens per workgroup and every expert; wavefront w owns expert blocks w, w + 4 (EBW of them,
+// E padded to 128 * EBW). Per 64-k step the buffer->LDS DMA brings x[64 tokens][64 k] (bf16,
+// 128-byte rows) and Wg[experts][64 k] (fp32, 256-byte rows) into a ring of NS stages, whole cache
+// lines per request. Each wavefront reads its experts' fp32 values from LDS (32 bytes per lane per
+// 16-k slice), splits them exactly into three bf16 parts in registers (split3), and runs the
+// three part MFMAs against both token blocks. A wavefront sums its whole contraction in k order
+// in one accumulator, so there is no cross-wavefront reduction and the result is deterministic.
+// The x rows are read from HBM once; Wg (at most 4 MiB) comes from L2 for every workgroup.
+constexpr int kLgDmaTok = 64;
+constexpr int kLgDmaMinT = 16384;   // from this many tokens (256 workgroups of 64)
+
+template <int EBW>
+struct LgDma {
+  static constexpr int EP = 32 * 4 * EBW;            // experts covered (padded)
+  static constexpr int X_BYTES = kLgDmaTok * 128;    // 8 KiB
+  static constexpr int W_BYTES = EP * 256;           // 32 or 64 KiB
+  static constexpr int STAGE = X_BYTES + W_BYTES;
+  static constexpr int NS = EBW == 1 ? 4 : 2;        // ring slots
+  static constexpr int LX = X_BYTES / 4096, LW = W_BYTES / 4096, L = LX + LW;   // per wavefront
+  static_assert(NS * STAGE <= 163840, "LDS budget");
+  static_assert(NS <= 5 && (NS - 1) * L < 64, "vmcnt range");
+};
+
+template <int EBW>
+__global__ __launch_bounds__(256, 1) void router_logits_dma_kernel(
+    int T, int H, int E, const uint16_t* __restrict__ x, const float* __restrict__ wg,
+    const float* __restrict__ logit_bias, float* __restrict__ logits) {
+  typedef LgDma<EBW> C;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NS * C::STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = (int)uniform((uint32_t)(threadIdx.x >> 6));
+  const int t0 = blockIdx.x * kLgDmaTok;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
+  // x rows t0.. (rows past T read as zero), all of Wg (rows past E read as zero)
+  const v4u32_t rx = make_rsrc(x + (int64_t)t0 * H, (int64_t)(T - t0) * H * 2);
+  const v4u32_t rw = make_rsrc(wg, (int64_t)E * H * 4);
+  // x: instruction i of wavefront w fills token rows (4 i + w) * 8 + lane / 8, 16-byte chunk
+  // position lane % 8 holding chunk c = position ^ ((row >> 1) & 7) (rows step by 32 between
+  // instructions, which keeps that swizzle). Wg: instruction j fills expert rows (4 j + w) * 4 +
+  // lane / 16, position lane % 16 holding chunk position ^ (row & 15) (rows step by 16).
+  const int xr = wave * 8 + lane / 8, xc = (lane % 8) ^ ((xr >> 1) & 7);
+  const uint32_t xoff = (uint32_t)(((int64_t)xr * H + xc * 8) * 2);
+  const int wr = wave * 4 + lane / 16, wc = (lane % 16) ^ (wr & 15);
+  const uint32_t woff = (uint32_t)(((int64_t)wr * H + wc * 4) * 4);
+  auto issue = [&](int kt, int slot) {
+    const uint32_t sl = lds_base + slot * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::LX; ++i)
+      dma16(rx, xoff + uniform((uint32_t)(kt * 128 + i * 32 * H * 2)), sl + (i * 4 + wave) * 1024);
+#pragma unroll
+    for (int j = 0; j < C::LW; ++j)
+      dma16(rw, woff + uniform((uint32_t)(kt * 256 + j * 16 * H * 4)),
+            sl + C::X_BYTES + (j * 4 + wave) * 1024);
+  };
+  f32x16_t acc[EBW][2];
+#pragma unroll
+  for (int e = 0; e < EBW; ++e)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[e][b][q] = 0.0f;
+  const int r = lane & 31, h = lane >> 5;
+  const int nst = H / 64;
+  for (int s = 0; s < C::NS - 1 && s < nst; ++s) issue(s, s);
+  for (int kt = 0; kt < nst; ++kt) {
+    // this wavefront's DMA of stage kt has landed (at most NS - 2 later stages are in flight);
+    // the barrier makes that true for all, and frees the slot every wavefront used at kt - 1
+    wait_stages<C::L, C::NS - 2>(min(C::NS - 2, nst - 1 - kt));
+    block_barrier();
+    if (kt + C::NS - 1 < nst) issue(kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
+    const unsigned char* sx = smem + (kt % C::NS) * C::STAGE;
+    const unsigned char* sw = sx + C::X_BYTES;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      bf16x8_t xf[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int row = b * 32 + r;
+        xf[b] = *reinterpret_cast<const bf16x8_t*>(sx + row * 128 + kswz64(row, 2 * sl + h) * 16);
+      }
+#pragma unroll
+      for (int e = 0; e < EBW; ++e) {
+        const int row = (wave + 4 * e) * 32 + r;
+        const int c0 = 4 * sl + 2 * h;
+        const float4 w0 = *reinterpret_cast<const float4*>(sw + row * 256 + ((c0 ^ (row & 15)) * 16));
+        const float4 w1 =
+            *reinterpret_cast<const float4*>(sw + row * 256 + (((c0 + 1) ^ (row & 15)) * 16));
+        bf16x8_t whi, wmid, wlo;
+        split3(w0, w1, whi, wmid, wlo);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)   // smallest part first
+          acc[e][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wlo, xf[b], acc[e][b], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[e][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wmid, xf[b], acc[e][b], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[e][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(whi, xf[b], acc[e][b], 0, 0, 0);
+      }
+    }
+  }
+  // D[expert][token]: lane -> token 32 b + r, register q -> expert 8 (q / 4) + 4 h + q % 4
+#pragma unroll
+  for (int e = 0; e < EBW; ++e)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int t = t0 + 32 * b + r;
+      if (t >= T) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e4 = (wave + 4 * e) * 32 + 8 * g + 4 * h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ee = e4 + q;
+          if (ee < E) {
+            float z = acc[e][b][4 * g + q];
+            if (logit_bias) z += logit_bias[ee];
+            logits[(int64_t)t * E + ee] = z;
+          }
+        }
+      }
+    }
 }
 
 // ---- 2. softmax, biased top-K, weights, counts -----------------------------------------------------
@@ -319,7 +449,13 @@ hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg
   }
   if (x) {
     const unsigned ge = (unsigned)((s.E + kLgTile - 1) / kLgTile);
-    if (s.T >= 4 * kLgLargeT)
+    if (s.T >= kLgDmaMinT && s.E <= 128)
+      hipLaunchKernelGGL((router_logits_dma_kernel<1>), dim3((unsigned)((s.T + kLgDmaTok - 1) / kLgDmaTok)),
+                         dim3(256), 0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
+    else if (s.T >= kLgDmaMinT)
+      hipLaunchKernelGGL((router_logits_dma_kernel<2>), dim3((unsigned)((s.T + kLgDmaTok - 1) / kLgDmaTok)),
+                         dim3(256), 0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
+    else if (s.T >= 4 * kLgLargeT)
       hipLaunchKernelGGL((router_logits_kernel<4, 4>), dim3((unsigned)((s.T + 127) / 128), ge), dim3(256),
                          0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
     else if (s.T >= kLgLargeT)

@@ -79,9 +79,14 @@ def test_route_logits_input():
     np.testing.assert_allclose(_np(w), vw, rtol=0, atol=1e-6)
 
 
-@pytest.mark.parametrize("name,T", [("c1", None), ("c3", 2048), ("c5", None), ("c5e", None)])
-def test_route_from_x(name, T):
-    cfg = get_config(name) if T is None else get_config(name, T=T)
+@pytest.mark.parametrize("name,T,over", [
+    ("c1", None, {}), ("c3", 2048, {}), ("c5", None, {}), ("c5e", None, {}),
+    # from 16384 tokens the logits kernel stages x and Wg in LDS (64 tokens per workgroup, all
+    # experts): a ragged last token tile, and 200 experts (two expert blocks per wavefront, a
+    # ragged last block)
+    ("c3", 16384 + 77, {}), ("c3", 16400, {"E": 200, "K": 8})])
+def test_route_from_x(name, T, over):
+    cfg = get_config(name, **over) if T is None else get_config(name, T=T, **over)
     log(f"route from x: {cfg}")
     x, wg, sb, lb = draw_x(cfg), draw_wg(cfg), draw_sel_bias(cfg), draw_logit_bias(cfg)
     s = _shape(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.S, cfg.block_m)
