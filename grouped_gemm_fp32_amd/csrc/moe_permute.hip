@@ -9,7 +9,8 @@
 // histograms, whose results do not depend on order):
 //   1. hist:    per token block, per-expert counts                        -> ws[nblk][E]
 //   2. segment: one workgroup scans ws per expert (block bases, counts), pads and prefix-sums the
-//               group sizes (seg_offsets, total_rows), fills tile_group and marks padding rows
+//               group sizes (seg_offsets, total_rows) and fills tile_group
+//      clear:   row_token = -1 on every row below total_rows (grid-wide)
 //   3. scatter: per token block, a [E][TB/32] bit mask of "token routed to e" gives each slot its
 //               stable rank (popcounts), hence pos[t,j] and row_token
 //   4. gather:  x_perm[r] = x[row_token[r]] or 0, 16-byte vector copies, rows < total_rows.
@@ -118,13 +119,17 @@ __global__ __launch_bounds__(kSegThreads) void perm_segment_kernel(
     }
     tile_group[i] = g;
   }
-  // Every row of every segment starts as padding (-1); the scatter then writes the token of each
-  // routed and shared row. With valid routing that leaves -1 exactly on the padding rows; with
-  // out-of-range or repeated expert indices (which the contract excludes) a row no slot claims
-  // stays -1 instead of holding whatever the buffer held.
-  const int lane = tid & 63, wave = tid >> 6;
-  for (int g = wave; g < G; g += kSegThreads / 64)
-    for (int r = seg[g] + lane; r < seg[g + 1]; r += 64) row_token[r] = -1;
+}
+
+// Every row below total_rows starts as padding (-1); the scatter then writes the token of each
+// routed and shared row. With valid routing that leaves -1 exactly on the padding rows; with
+// out-of-range or repeated expert indices (which the contract excludes) a row no slot claims
+// stays -1 instead of holding whatever the buffer held. Rows from total_rows on are not written.
+__global__ __launch_bounds__(kThreads) void perm_clear_rows_kernel(int64_t mcap,
+                                                                   const int32_t* __restrict__ total,
+                                                                   int32_t* __restrict__ row_token) {
+  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (r < mcap && r < total[0]) row_token[r] = -1;
 }
 
 __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
@@ -239,6 +244,8 @@ hipError_t launch_permute(const moe_shape_t& s, int64_t mcap, const int32_t* top
   }
   hipLaunchKernelGGL(perm_segment_kernel, dim3(1), dim3(kSegThreads), seg_lds, st, s.T, s.E, s.S,
                      s.block_m, nblk, mcap, ws, seg_offsets, tile_group, total_rows, row_token);
+  hipLaunchKernelGGL(perm_clear_rows_kernel, dim3((unsigned)((mcap + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, mcap, total_rows, row_token);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(nblk), dim3(kThreads), sc_lds, st, s.T, s.K, s.E,
                      s.S, TB, topk_idx, ws, seg_offsets, pos, row_token);
   if (x) {

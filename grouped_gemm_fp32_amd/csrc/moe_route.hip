@@ -13,7 +13,9 @@
 //      wavefronts split the 64-k steps and their partial sums are added in wavefront order.
 //   2. route_kernel, one wavefront per token at a time (a few consecutive tokens each): softmax
 //      over E, key = p + b, K rounds of a wave-wide arg-max on a 64-bit (key, index) code,
-//      weights, per-expert counts (an LDS histogram per workgroup, then one atomic per expert).
+//      weights.
+//   3. count_kernel: per-expert counts of the selected slots, 16 experts x one chunk of topk_idx
+//      per workgroup, summed with one integer atomic per expert and chunk.
 //      The cross-lane reductions use DPP and permlane swaps, not the LDS crossbar.
 #include "moe_common.h"
 #include "moe_dma.h"
@@ -129,16 +131,18 @@ __global__ __launch_bounds__(NW * 64) void router_logits_kernel(
 __device__ __forceinline__ int kswz64(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // ---- 1b. router logits for large batches, operands staged in LDS ---------------------------------
-// 64 tokens per workgroup and every expert; wavefront w owns expert blocks w, w + 4 (EBW of them,
-// E padded to 128 * EBW). Per 64-k step the buffer->LDS DMA brings x[64 tokens][64 k] (bf16,
-// 128-byte rows) and Wg[experts][64 k] (fp32, 256-byte rows) into a ring of NS stages, whole cache
-// lines per request. Each wavefront reads its experts' fp32 values from LDS (32 bytes per lane per
-// 16-k slice), splits them exactly into three bf16 parts in registers (split3), and runs the
-// three part MFMAs against both token blocks. A wavefront sums its whole contraction in k order
-// in one accumulator, so there is no cross-wavefront reduction and the result is deterministic.
-// The x rows are read from HBM once; Wg (at most 4 MiB) comes from L2 for every workgroup.
+// 64 tokens per workgroup and every expert (E padded to 128 * EBW). Per 64-k step the buffer->LDS
+// DMA brings x[64 tokens][64 k] (bf16, 128-byte rows) and Wg[experts][64 k] (fp32, 256-byte rows)
+// into a ring of NS stages, whole cache lines per request. Eight wavefronts, two per SIMD: wave
+// w takes expert blocks (w & 3) + 4 e for both token blocks, waves 0-3 the first two 16-k slices
+// of every step and waves 4-7 the last two. A wavefront reads its experts' fp32 values from LDS
+// (32 bytes per lane per slice), splits them exactly into three bf16 parts in registers (split3)
+// and runs the three part MFMAs against both token blocks. At the end waves 4-7 hand their sums
+// to waves 0-3 through LDS, which add them in that fixed order, so the result is deterministic.
+// x is read from HBM once; Wg (at most 4 MiB) comes from L2 for every workgroup.
 constexpr int kLgDmaTok = 64;
 constexpr int kLgDmaMinT = 16384;   // from this many tokens (256 workgroups of 64)
+constexpr int kLgDmaThreads = 512;
 
 template <int EBW>
 struct LgDma {
@@ -147,28 +151,33 @@ struct LgDma {
   static constexpr int W_BYTES = EP * 256;           // 32 or 64 KiB
   static constexpr int STAGE = X_BYTES + W_BYTES;
   static constexpr int NS = EBW == 1 ? 4 : 2;        // ring slots
-  static constexpr int LX = X_BYTES / 4096, LW = W_BYTES / 4096, L = LX + LW;   // per wavefront
+  static constexpr int NW = kLgDmaThreads / 64;
+  static constexpr int LX = X_BYTES / (NW * 1024), LW = W_BYTES / (NW * 1024), L = LX + LW;
   static_assert(NS * STAGE <= 163840, "LDS budget");
   static_assert(NS <= 5 && (NS - 1) * L < 64, "vmcnt range");
+  static_assert(X_BYTES % (NW * 1024) == 0 && W_BYTES % (NW * 1024) == 0, "whole DMA rounds");
+  static_assert(4 * EP * kLgDmaTok <= NS * STAGE, "the hand-over of the partial sums fits");
 };
 
 template <int EBW>
-__global__ __launch_bounds__(256, 1) void router_logits_dma_kernel(
+__global__ __launch_bounds__(kLgDmaThreads, 1) void router_logits_dma_kernel(
     int T, int H, int E, const uint16_t* __restrict__ x, const float* __restrict__ wg,
     const float* __restrict__ logit_bias, float* __restrict__ logits) {
   typedef LgDma<EBW> C;
+  constexpr int NW = C::NW;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NS * C::STAGE];
   const int lane = threadIdx.x & 63;
   const int wave = (int)uniform((uint32_t)(threadIdx.x >> 6));
+  const int eb0 = wave & 3, half = wave >> 2;
   const int t0 = blockIdx.x * kLgDmaTok;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
   // x rows t0.. (rows past T read as zero), all of Wg (rows past E read as zero)
   const v4u32_t rx = make_rsrc(x + (int64_t)t0 * H, (int64_t)(T - t0) * H * 2);
   const v4u32_t rw = make_rsrc(wg, (int64_t)E * H * 4);
-  // x: instruction i of wavefront w fills token rows (4 i + w) * 8 + lane / 8, 16-byte chunk
-  // position lane % 8 holding chunk c = position ^ ((row >> 1) & 7) (rows step by 32 between
-  // instructions, which keeps that swizzle). Wg: instruction j fills expert rows (4 j + w) * 4 +
-  // lane / 16, position lane % 16 holding chunk position ^ (row & 15) (rows step by 16).
+  // x: instruction i of wavefront w fills token rows (NW i + w) * 8 + lane / 8, 16-byte chunk
+  // position lane % 8 holding chunk position ^ ((row >> 1) & 7) (rows step by 64 between
+  // instructions, which keeps that swizzle). Wg: instruction j fills expert rows (NW j + w) * 4 +
+  // lane / 16, position lane % 16 holding chunk position ^ (row & 15) (rows step by 32).
   const int xr = wave * 8 + lane / 8, xc = (lane % 8) ^ ((xr >> 1) & 7);
   const uint32_t xoff = (uint32_t)(((int64_t)xr * H + xc * 8) * 2);
   const int wr = wave * 4 + lane / 16, wc = (lane % 16) ^ (wr & 15);
@@ -177,11 +186,12 @@ __global__ __launch_bounds__(256, 1) void router_logits_dma_kernel(
     const uint32_t sl = lds_base + slot * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::LX; ++i)
-      dma16(rx, xoff + uniform((uint32_t)(kt * 128 + i * 32 * H * 2)), sl + (i * 4 + wave) * 1024);
+      dma16(rx, xoff + uniform((uint32_t)(kt * 128 + i * NW * 8 * H * 2)),
+            sl + (i * NW + wave) * 1024);
 #pragma unroll
     for (int j = 0; j < C::LW; ++j)
-      dma16(rw, woff + uniform((uint32_t)(kt * 256 + j * 16 * H * 4)),
-            sl + C::X_BYTES + (j * 4 + wave) * 1024);
+      dma16(rw, woff + uniform((uint32_t)(kt * 256 + j * NW * 4 * H * 4)),
+            sl + C::X_BYTES + (j * NW + wave) * 1024);
   };
   f32x16_t acc[EBW][2];
 #pragma unroll
@@ -202,7 +212,8 @@ __global__ __launch_bounds__(256, 1) void router_logits_dma_kernel(
     const unsigned char* sx = smem + (kt % C::NS) * C::STAGE;
     const unsigned char* sw = sx + C::X_BYTES;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int sl = 2 * half + s2;
       bf16x8_t xf[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -211,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void router_logits_dma_kernel(
       }
 #pragma unroll
       for (int e = 0; e < EBW; ++e) {
-        const int row = (wave + 4 * e) * 32 + r;
+        const int row = (eb0 + 4 * e) * 32 + r;
         const int c0 = 4 * sl + 2 * h;
         const float4 w0 = *reinterpret_cast<const float4*>(sw + row * 256 + ((c0 ^ (row & 15)) * 16));
         const float4 w1 =
@@ -230,30 +241,41 @@ __global__ __launch_bounds__(256, 1) void router_logits_dma_kernel(
       }
     }
   }
+  // waves 4-7 hand their partial sums (the last two slices of every step) to waves 0-3
+  float* hand = reinterpret_cast<float*>(smem);   // [4][EBW][2][16][64]
+  wait_lgkm0();
+  block_barrier();
+  if (half) {
+#pragma unroll
+    for (int e = 0; e < EBW; ++e)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) hand[(((eb0 * EBW + e) * 2 + b) * 16 + q) * 64 + lane] = acc[e][b][q];
+  }
+  __syncthreads();
+  if (half) return;
   // D[expert][token]: lane -> token 32 b + r, register q -> expert 8 (q / 4) + 4 h + q % 4
 #pragma unroll
   for (int e = 0; e < EBW; ++e)
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int t = t0 + 32 * b + r;
-      if (t >= T) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int e4 = (wave + 4 * e) * 32 + 8 * g + 4 * h;
+        const int e4 = (eb0 + 4 * e) * 32 + 8 * g + 4 * h;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int ee = e4 + q;
-          if (ee < E) {
-            float z = acc[e][b][4 * g + q];
-            if (logit_bias) z += logit_bias[ee];
-            logits[(int64_t)t * E + ee] = z;
-          }
+          const float z0 = acc[e][b][4 * g + q] +
+                           hand[(((eb0 * EBW + e) * 2 + b) * 16 + 4 * g + q) * 64 + lane];
+          if (t < T && ee < E) logits[(int64_t)t * E + ee] = logit_bias ? z0 + logit_bias[ee] : z0;
         }
       }
     }
 }
 
-// ---- 2. softmax, biased top-K, weights, counts -----------------------------------------------------
+// ---- 2. softmax, biased top-K, weights -----------------------------------------------------------
 // Cross-lane steps without the LDS crossbar: DPP for partners within a row of 16 lanes, and
 // gfx950's permlane swaps for rows 16 and 32 apart. Each step combines two disjoint, equal-size
 // lane groups that are already uniform, so after six steps every lane holds the reduction over
@@ -309,13 +331,10 @@ template <int MODE>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     int T, int E, int K, int tpw, uint32_t flags, const float* __restrict__ sel_bias,
     const float* __restrict__ logits, float* __restrict__ probs, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int32_t* __restrict__ counts) {
-  __shared__ int hist[kMaxE];
+    float* __restrict__ topk_w) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  for (int e = tid; e < E; e += kRouteThreads) hist[e] = 0;
-  __syncthreads();
 
   const bool norm = (flags & MOE_NORM_TOPK) != 0;
   const float* src = MODE == kFromLogits ? logits : probs;
@@ -406,13 +425,61 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         if (j == lane) { pe = sel_p[j]; e = sel_e[j]; }
       topk_idx[(int64_t)t * K + lane] = e;
       topk_w[(int64_t)t * K + lane] = norm ? pe / wsum : pe;
-      if (counts) atomicAdd(&hist[e], 1);
     }
   }
+}
+
+// ---- 3. expert counts ---------------------------------------------------------------------------
+// counts[e] = number of (token, slot) pairs routed to e. Workgroup (g, c) counts experts
+// 16 g .. 16 g + 15 over chunk c of topk_idx (2048 entries, 8 per lane, read as two 16-byte
+// loads in flight together): each lane keeps 16 counters, the workgroup sums them, and one integer
+// atomic per expert and chunk adds the result (a few dozen per address, where an atomic per expert
+// from every routing workgroup piled up on the busiest experts). Integer sums do not depend on
+// order, so the counts are exact and deterministic.
+constexpr int kCntExperts = 16;
+constexpr int kCntThreads = 256;
+constexpr int kCntPer = 8;                                      // entries per lane
+constexpr int64_t kCntChunk = (int64_t)kCntThreads * kCntPer;   // entries per workgroup
+
+__global__ __launch_bounds__(kCntThreads) void count_kernel(int64_t n, int E,
+                                                            const int32_t* __restrict__ idx,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ int part[kCntThreads / 64][kCntExperts];
+  const int e0 = blockIdx.x * kCntExperts;
+  const int64_t i0 = (int64_t)blockIdx.y * kCntChunk + (int64_t)threadIdx.x * kCntPer;
+  int v[kCntPer];
+  if (i0 + kCntPer <= n && (((uintptr_t)(idx + i0)) & 15) == 0) {
+    const int4 a = *reinterpret_cast<const int4*>(idx + i0);
+    const int4 b = *reinterpret_cast<const int4*>(idx + i0 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int u = 0; u < kCntPer; ++u) v[u] = i0 + u < n ? idx[i0 + u] : -1;
+  }
+  int c[kCntExperts];
+#pragma unroll
+  for (int j = 0; j < kCntExperts; ++j) c[j] = 0;
+#pragma unroll
+  for (int u = 0; u < kCntPer; ++u) {
+    const int d = v[u] - e0;
+#pragma unroll
+    for (int j = 0; j < kCntExperts; ++j) c[j] += d == j;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < kCntExperts; ++j) {
+    int x = c[j];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    if (lane == 0) part[wave][j] = x;
+  }
   __syncthreads();
-  if (counts)
-    for (int e = tid; e < E; e += kRouteThreads)
-      if (hist[e]) atomicAdd(&counts[e], hist[e]);
+  if (threadIdx.x < kCntExperts && e0 + (int)threadIdx.x < E) {
+    int x = 0;
+#pragma unroll
+    for (int w = 0; w < kCntThreads / 64; ++w) x += part[w][threadIdx.x];
+    if (x) atomicAdd(&counts[e0 + threadIdx.x], x);
+  }
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
@@ -429,6 +496,20 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+namespace {
+// counts were cleared before the routing kernels ran (fill_i32_kernel)
+hipError_t launch_counts(const moe_shape_t& s, const int32_t* topk_idx, int32_t* counts,
+                         hipStream_t st) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !counts) return e;
+  const int64_t n = (int64_t)s.T * s.K;
+  const dim3 grid((unsigned)((s.E + kCntExperts - 1) / kCntExperts),
+                  (unsigned)((n + kCntChunk - 1) / kCntChunk));
+  hipLaunchKernelGGL(count_kernel, grid, dim3(kCntThreads), 0, st, n, s.E, topk_idx, counts);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg,
                         const float* logit_bias, const float* sel_bias, float* logits,
                         float* probs, int32_t* topk_idx, float* topk_w, int32_t* counts,
@@ -444,17 +525,17 @@ hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg
   const dim3 grid((unsigned)((s.T + toks_per_wg - 1) / toks_per_wg)), block(kRouteThreads);
   if (s.flags & MOE_PROBS_IN) {
     hipLaunchKernelGGL(route_kernel<kFromProbs>, grid, block, 0, st, s.T, s.E, s.K, tpw, s.flags,
-                       sel_bias, logits, probs, topk_idx, topk_w, counts);
-    return hipGetLastError();
+                       sel_bias, logits, probs, topk_idx, topk_w);
+    return launch_counts(s, topk_idx, counts, st);
   }
   if (x) {
     const unsigned ge = (unsigned)((s.E + kLgTile - 1) / kLgTile);
     if (s.T >= kLgDmaMinT && s.E <= 128)
       hipLaunchKernelGGL((router_logits_dma_kernel<1>), dim3((unsigned)((s.T + kLgDmaTok - 1) / kLgDmaTok)),
-                         dim3(256), 0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
+                         dim3(kLgDmaThreads), 0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
     else if (s.T >= kLgDmaMinT)
       hipLaunchKernelGGL((router_logits_dma_kernel<2>), dim3((unsigned)((s.T + kLgDmaTok - 1) / kLgDmaTok)),
-                         dim3(256), 0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
+                         dim3(kLgDmaThreads), 0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
     else if (s.T >= 4 * kLgLargeT)
       hipLaunchKernelGGL((router_logits_kernel<4, 4>), dim3((unsigned)((s.T + 127) / 128), ge), dim3(256),
                          0, st, s.T, s.H, s.E, x, wg, logit_bias, logits);
@@ -468,8 +549,8 @@ hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(route_kernel<kFromLogits>, grid, block, 0, st, s.T, s.E, s.K, tpw, s.flags,
-                     sel_bias, logits, probs, topk_idx, topk_w, counts);
-  return hipGetLastError();
+                     sel_bias, logits, probs, topk_idx, topk_w);
+  return launch_counts(s, topk_idx, counts, st);
 }
 
 }  // namespace moe

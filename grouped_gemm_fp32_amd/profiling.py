@@ -63,8 +63,11 @@ OUTSIDE_STEP = {
 
 # Other kernels of a stage (labels only: STAGE_OF keeps one kernel per stage for the traffic table).
 PART_OF = {
-    "router_logits_kernel<2,4>": "route (router logits)", "router_logits_kernel<1,8>": "route (router logits)",
-    "fill_i32_kernel": "route (count clear)",
+    "router_logits_kernel<4,4>": "route (router logits)", "router_logits_kernel<2,4>": "route (router logits)",
+    "router_logits_kernel<1,8>": "route (router logits)",
+    "router_logits_dma_kernel<1>": "route (router logits)", "router_logits_dma_kernel<2>": "route (router logits)",
+    "fill_i32_kernel": "route (count clear)", "count_kernel": "route (expert counts)",
+    "perm_clear_rows_kernel": "permute (maps)",
     "perm_hist_kernel": "permute (segments)", "perm_segment_kernel": "permute (segments)",
     "perm_scatter_kernel": "permute (maps)", "zero_pad_rows_kernel": "combine_bwd (padding rows)",
     "ggemm_kernel<0,16,256,16,1>": "fwd_gateup (16-row tiles)",
