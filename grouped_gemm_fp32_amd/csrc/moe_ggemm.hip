@@ -885,7 +885,7 @@ __device__ __forceinline__ void store_tile8(const GemmArgs& p, const f32x16_t (&
 // ------------------------------------------------------------------------------------------------
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile8 {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = 8, BK = 64, KK = 4;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = 8, BK = 64, KK = 4, NS = 2;
   static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
   static constexpr int LA = A_BYTES / (NW * 1024), LB = B_BYTES / (NW * 1024), L = LA + LB;
@@ -893,7 +893,7 @@ struct Tile8 {
   static constexpr int P1 = (L + 2) / 3, P2 = (2 * L + 2) / 3;
   static_assert(WM * WN == NW && TM * 32 == WTM && TN * 32 == WTN, "wave tiling");
   static_assert(A_BYTES % (NW * 1024) == 0 && B_BYTES % (NW * 1024) == 0, "whole DMA rounds");
-  static_assert(2 * STAGE <= kLdsBytes, "two stages must fit in LDS");
+  static_assert(NS * STAGE <= kLdsBytes, "two stages must fit in LDS");
 };
 constexpr int kThreads8 = 512;
 
@@ -1062,21 +1062,27 @@ struct Eng8 {
     if (Tr::split) return (j / (TN / 2)) * (BN / 2) + wn * (WTN / 2) + (j % (TN / 2)) * 32;
     return wn * WTN + j * 32;
   }
+  // K-major: row0 is a multiple of 32, so the row swizzle (r >> 1) & 7 depends on the lane only
+  // and slice kk flips bits 5-6 of the lane's offset: one lane offset serves every fragment and
+  // slice, the rest is wave-uniform.
+  __device__ __forceinline__ uint32_t lane_k() const {
+    const int r = lane & 31;
+    return (uint32_t)(r * (BK * 2) + (((lane >> 5) ^ ((r >> 1) & 7)) << 4));
+  }
   __device__ __forceinline__ bf16x8_t frag_k(int base, int row0, int kk) const {
-    const int r = row0 + (lane & 31);
-    return *reinterpret_cast<const bf16x8_t*>(smem + base + r * (BK * 2) +
-                                              kswz<BK>(r, 2 * kk + (lane >> 5)) * 16);
+    return *reinterpret_cast<const bf16x8_t*>(smem + base + row0 * (BK * 2) + (lane_k() ^ (kk << 5)));
   }
   // MN-major: two transposed 8-byte reads give columns col0 + (grp&1)*16 + li,
-  // k = kk*16 + (grp>>1)*8 + 0..7.
+  // k = kk*16 + (grp>>1)*8 + 0..7. The k-row swizzle uses k & 3, which does not depend on kk, so
+  // kk only adds a wave-uniform 32 * rows bytes to a per-fragment lane offset.
   __device__ __forceinline__ bf16x8_t frag_t(int base, int rows, int col0, int kk) const {
     const int grp = lane >> 4, li = lane & 15;
     const int col = col0 + (grp & 1) * 16 + 4 * (li & 3);
     const int cc = col >> 3, half = ((col >> 2) & 1) * 8;
-    const int k0 = kk * 16 + (grp >> 1) * 8 + (li >> 2);
-    const int ad0 = base + k0 * rows * 2 + ((cc ^ ((k0 & 3) << 2)) * 16) + half;
-    const int k1 = k0 + 4;
-    const int ad1 = base + k1 * rows * 2 + ((cc ^ ((k1 & 3) << 2)) * 16) + half;
+    const int kl = (grp >> 1) * 8 + (li >> 2);
+    const int lo_off = kl * rows * 2 + ((cc ^ ((kl & 3) << 2)) * 16) + half;
+    const int ad0 = base + kk * 32 * rows + lo_off;
+    const int ad1 = ad0 + 8 * rows;   // k + 4
     const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(s3 + ad0));
     const v4i16_t hi2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(s3 + ad1));
     bf16x8_t r;
@@ -1084,28 +1090,34 @@ struct Eng8 {
     __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi2, 8);
     return r;
   }
-  __device__ __forceinline__ void load(int slot, int kk, Frags& f) const {
-    if (kRagged && !mma_on) return;
+  // Fragment q of slice kk (q < TM: A block q, else B block q - TM).
+  __device__ __forceinline__ void load_one(int slot, int kk, int q, Frags& f) const {
     const int sa = slot * STAGE, sb = sa + A_BYTES;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if constexpr (AMN) f.a[i] = frag_t(sa, BM, wm * WTM + i * 32, kk);
-      else f.a[i] = frag_k(sa, wm * WTM + i * 32, kk);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      if constexpr (BMN) f.b[j] = frag_t(sb, BN, b_row(j), kk);
-      else f.b[j] = frag_k(sb, b_row(j), kk);
+    if (q < TM) {
+      if constexpr (AMN) f.a[q] = frag_t(sa, BM, wm * WTM + q * 32, kk);
+      else f.a[q] = frag_k(sa, wm * WTM + q * 32, kk);
+    } else {
+      if constexpr (BMN) f.b[q - TM] = frag_t(sb, BN, b_row(q - TM), kk);
+      else f.b[q - TM] = frag_k(sb, b_row(q - TM), kk);
     }
   }
-  // The slice's MFMAs with DMA instructions [D0, D1) of stage kt_dma of tile st spread evenly
-  // among them.
-  // With nd < D1 - D0 only the first nd of them are issued.
-  template <int D0, int D1>
+  __device__ __forceinline__ void load(int slot, int kk, Frags& f) const {
+#pragma unroll
+    for (int q = 0; q < TM + TN; ++q) load_one(slot, kk, q, f);
+  }
+  // The slice's MFMAs (A block i against B blocks 0..TN-1, i = 0..TM-1) with DMA instructions
+  // [D0, D1) of stage kt_dma of tile st spread evenly among them; with nd < D1 - D0 only the first
+  // nd of them are issued. With `nxt` the fragments of the next slice (kk_n of slot_n) are read
+  // into fn as those of this one die: A block i after its last MFMA (row i done), B block j after
+  // the last row's MFMA with it. So the next slice's first MFMAs find their operands in registers
+  // instead of starting with a full LDS round trip.
+  // ACT false: a wave with nothing to compute in this tile issues only its DMA share.
+  template <int D0, int D1, bool ACT>
   __device__ __forceinline__ void mma_dma(Acc& acc, const Frags& f, bool on, const Dma& st,
-                                          int kt_dma, int slot_dma, int nd = D1 - D0) const {
+                                          int kt_dma, int slot_dma, Frags& fn, int slot_n, int kk_n,
+                                          bool nxt, int nd = D1 - D0) const {
     constexpr int N = D1 - D0, T = TM * TN;
-    if (kRagged && !mma_on) {   // nothing to compute in this tile: only this wave's DMA share
+    if constexpr (!ACT) {
       if constexpr (N > 0) {
 #pragma unroll
         for (int d = 0; d < N; ++d)
@@ -1125,6 +1137,13 @@ struct Eng8 {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       acc[t / TN][t % TN] = Mf::run(f.b[t % TN], f.a[t / TN], acc[t / TN][t % TN]);
+      if (nxt && (t % TN == TN - 1 || t / TN == TM - 1)) {
+        // kept in place: read earlier, a fragment would need registers of its own
+        __builtin_amdgcn_sched_barrier(0);
+        if (t % TN == TN - 1) load_one(slot_n, kk_n, t / TN, fn);
+        if (t / TN == TM - 1) load_one(slot_n, kk_n, TM + t % TN, fn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if constexpr (N > 0 && HD) {
         constexpr int N2 = 2 * N;
 #pragma unroll
@@ -1163,10 +1182,61 @@ struct Eng8 {
   // and its stage 1 in full during the last slice, so on return the next tile meets the entry
   // condition above with s0' = (s0 + nk) & 1. Without it, at_end() runs once in the last stage,
   // after this wave's last fragment reads are issued and before the last slice's MFMAs.
+  // Fragments alternate between two sets: slice kk computes from one while the other receives
+  // slice kk + 1 (the next stage's slice 0 after the barrier that makes that stage visible).
+  // A wave whose columns of the tile all lie past N (mma_on false) runs the same schedule of DMA
+  // and barriers without fragment reads or MFMAs, in a loop of its own, so that neither path
+  // keeps the other's registers live.
   template <int S, bool CHAIN, class AtEnd>
   __device__ __forceinline__ void run(Acc& acc, const Dma& cu, int nk, int s0, bool stores_pending,
                                       const Dma& nx, bool chain_, AtEnd at_end) {
+    if constexpr (kRagged) {
+      if (!mma_on) {
+        run_impl<S, CHAIN, false>(acc, cu, nk, s0, stores_pending, nx, chain_, at_end);
+        return;
+      }
+    }
+    run_impl<S, CHAIN, true>(acc, cu, nk, s0, stores_pending, nx, chain_, at_end);
+  }
+
+  // This wave's DMA instructions per stage (HD: waves 0-3 issue both halves, waves 4-7 none).
+  static constexpr int LW = HD ? 2 * L : L;
+  // Wait until the DMA of a stage has landed while the `later` stages issued after it (at most
+  // one: the ring has two slots) and, with st_out, the S stores issued after those may still be
+  // out. vmcnt counts in issue order.
+  template <int S>
+  __device__ __forceinline__ void wait_later(int later, bool st_out) const {
+    static_assert(!HD || S == 0, "the half-DMA kinds have no stores in flight");
+    static_assert(LW + S < 64, "vmcnt range");
+    if constexpr (HD) {
+      if (wave >= 4) return;   // issues no DMA
+    }
+    if (st_out) {
+      if constexpr (S > 0) {
+        if (later >= 1) wait_vm<LW + S>();
+        else wait_vm<S>();
+        return;
+      }
+    }
+    if (later >= 1) wait_vm<LW>();
+    else wait_vm<0>();
+  }
+  // The first min(NS, nk) stages of a tile, in full, into slots 0.. (the ring is free).
+  __device__ __forceinline__ int issue_first(const Dma& st, int nk) const {
+    const int n = min(TL::NS, nk);
+#pragma unroll
+    for (int s = 0; s < TL::NS; ++s)
+      if (s < n) issue_stage(st, s, s);
+    return n;
+  }
+
+  template <int S, bool CHAIN, bool ACT, class AtEnd>
+  __device__ __forceinline__ void run_impl(Acc& acc, const Dma& cu, int nk, int s0,
+                                           bool stores_pending, const Dma& nx, bool chain_,
+                                           AtEnd at_end) {
     const bool chain = CHAIN && chain_;
+    Frags f0, f1;
+    if constexpr (ACT) load(s0 & 1, 0, f0);
     for (int kt = 0; kt < nk; ++kt) {
       const int slot = (s0 + kt) & 1;
       // stage kt + 1: this tile's or (chain) the next tile's stage 0; its first DMA part was
@@ -1175,14 +1245,9 @@ struct Eng8 {
       const bool pend = kt >= 1 && (kt + 1 < nk || chain);
       const Dma& st1 = nx1 ? nx : cu;
       const int k1 = nx1 ? 0 : kt + 1;
-      Frags f;
-      load(slot, 0, f);
-      mma_dma<TL::P1, TL::P2>(acc, f, pend, st1, k1, slot ^ 1);
-      load(slot, 1, f);
-      mma_dma<TL::P2, L>(acc, f, pend, st1, k1, slot ^ 1);
-      load(slot, 2, f);
-      mma_dma<0, 0>(acc, f, false, cu, 0, 0);
-      load(slot, 3, f);
+      mma_dma<TL::P1, TL::P2, ACT>(acc, f0, pend, st1, k1, slot ^ 1, f1, slot, 1, true);
+      mma_dma<TL::P2, L, ACT>(acc, f1, pend, st1, k1, slot ^ 1, f0, slot, 2, true);
+      mma_dma<0, 0, ACT>(acc, f0, false, cu, 0, 0, f1, slot, 3, true);
       if (kt + 1 < nk || chain) {
         // This wave's DMA of stage kt + 1 has landed and its reads of this slot are done; the
         // barrier makes both true for every wave, so stage kt + 1 is visible and the slot free.
@@ -1191,16 +1256,20 @@ struct Eng8 {
         wait_lgkm0();
         block_barrier();
       }
+      // The next stage's slice 0 is read during this slice in every stage: in the last one the
+      // reads find whatever the other slot holds and are never used, but made conditional they
+      // would keep the old fragments live beside the new ones (a register spill in the loop).
+      constexpr bool nxt = true;
       if constexpr (!CHAIN) {
         if (kt + 1 == nk) at_end();
-        mma_dma<0, TL::P1>(acc, f, kt + 2 < nk, cu, kt + 2, slot);   // this tile's stage kt + 2
+        mma_dma<0, TL::P1, ACT>(acc, f1, kt + 2 < nk, cu, kt + 2, slot, f0, slot ^ 1, 0, nxt);
       } else {
         // stage kt + 2 of the stream: this tile's (first part), the next tile's stage 0 (first
         // part) or the next tile's stage 1 (whole, since that tile starts with it issued)
         if (kt + 1 == nk && !chain) at_end();
         const bool own = kt + 2 < nk;
-        mma_dma<0, L>(acc, f, own || chain, own ? cu : nx, own ? kt + 2 : kt + 2 - nk, slot,
-                      kt + 2 <= nk ? TL::P1 : L);
+        mma_dma<0, L, ACT>(acc, f1, own || chain, own ? cu : nx, own ? kt + 2 : kt + 2 - nk, slot,
+                      f0, slot ^ 1, 0, nxt, kt + 2 <= nk ? TL::P1 : L);
       }
     }
   }
@@ -1219,27 +1288,18 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
   E::zero(acc);
   const int nk = (klen + TL::BK - 1) / TL::BK;
   if (nk > 0) {
-    e.issue_stage(st, 0, 0);
-    if (nk > 1) {
-      e.issue_stage(st, 1, 1);
-      if constexpr (E::HD) {
-        if (e.wave < 4) wait_vm<2 * TL::L>();
-      } else {
-        wait_vm<TL::L>();
-      }
-    } else {
-      wait_vm<0>();
-    }
+    const int n = e.issue_first(st, nk);
+    e.template wait_later<0>(n - 1, false);   // stage 0 landed
     block_barrier();
     e.template run<0, false>(acc, st, nk, 0, false, st, false, [] {});
   }
-  // Every wavefront is done with the ring: the two stages become per-wavefront staging buffers.
-  static_assert(2 * TL::STAGE / TL::NW >= 8192, "8 KiB of LDS per wavefront for the epilogue");
+  // Every wavefront is done with the ring: its slots become per-wavefront staging buffers.
+  static_assert(TL::NS * TL::STAGE / TL::NW >= 8192, "8 KiB of LDS per wavefront for the epilogue");
   wait_lgkm0();
   block_barrier();
   if (E::kRagged && !e.mma_on) return;   // every column of this wave is at or past N
   store_tile8<KIND, TL::TM, TL::TN, TL::WTM, TL::WTN>(p, acc, g, m0, n0, e.wm, e.wn, e.lane,
-                                                      smem + e.wave * (2 * TL::STAGE / TL::NW));
+                                                      smem + e.wave * (TL::NS * TL::STAGE / TL::NW));
 }
 
 // Tall tiles on the eight-wavefront engine: 4 x 2 wavefronts over 256 columns (a ragged last
@@ -1326,8 +1386,9 @@ constexpr int kWgradScr = 4096;                     // epilogue staging per wave
 template <bool F32> constexpr int wgrad_stores() {
   return Wgrad8Tile::TM * (F32 ? Wgrad8Tile::TN : Wgrad8Tile::TN / 2) * 4;
 }
-static_assert(2 * Wgrad8Tile::STAGE + Wgrad8Tile::NW * kWgradScr <= kLdsBytes, "LDS budget");
-static_assert(Wgrad8Tile::L + wgrad_stores<true>() < 64, "vmcnt range");
+static_assert(Wgrad8Tile::NS * Wgrad8Tile::STAGE + Wgrad8Tile::NW * kWgradScr <= kLdsBytes,
+              "LDS budget");
+static_assert((Wgrad8Tile::NS - 1) * Wgrad8Tile::L + wgrad_stores<true>() < 64, "vmcnt range");
 
 // Epilogue with 32 x 64 (bf16) or 32 x 32 (fp32) staging passes and bounds-checked buffer stores:
 // lanes outside the weight matrix get an offset past the buffer's end, which the hardware drops,
@@ -1418,25 +1479,20 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) 
     return t;
   };
   E e(p, smem);
-  unsigned char* scr = smem + 2 * TL::STAGE + e.wave * kWgradScr;
+  constexpr int NS = TL::NS;
+  unsigned char* scr = smem + NS * TL::STAGE + e.wave * kWgradScr;
   typename E::Dma dc, dn;   // DMA state of the current and the next tile
   T cur = decode(l);
   e.setup(dc, cur.g, cur.m0, cur.n0, cur.kbeg, cur.klen);
-  if (cur.nk > 0) e.issue_stage(dc, 0, 0);
-  if (cur.nk > 1) e.issue_stage(dc, 1, 1);
+  e.issue_first(dc, cur.nk);
   int s0 = 0;             // slot of the current tile's stage 0
-  bool stores = false;    // this wave's previous-tile stores are queued after the first two stages
+  bool stores = false;    // this wave's previous-tile stores are queued after the first stages
   bool ready = false;     // the current tile's stage 0 is already visible (chained DMA)
   for (;;) {
     if (!ready) {
-      if (cur.nk > 0) {
-        // stage 0 of this tile has landed (stage 1 and the previous tile's stores may be out)
-        if (cur.nk > 1) {
-          if (stores) wait_vm<L + S>(); else wait_vm<L>();
-        } else {
-          if (stores) wait_vm<S>(); else wait_vm<0>();
-        }
-      }
+      // stage 0 of this tile has landed (the later first stages and the previous tile's stores
+      // may be out)
+      if (cur.nk > 0) e.template wait_later<S>(min(NS, cur.nk) - 1, stores);
       block_barrier();
     }
     typename E::Acc acc;
@@ -1451,21 +1507,18 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) 
     }
     // The next tile's first stages follow this tile's in the same DMA stream when both have at
     // least two; otherwise they are issued, whole, once every wave is done with the ring.
-    const bool chain = has_next && cur.nk >= 2 && nxt.nk >= 2;
+    const bool chain = has_next && cur.nk >= NS && nxt.nk >= NS;
     auto at_end = [&] {
       wait_lgkm0();
       block_barrier();
-      if (has_next) {
-        if (nxt.nk > 0) e.issue_stage(dn, 0, 0);
-        if (nxt.nk > 1) e.issue_stage(dn, 1, 1);
-      }
+      if (has_next) e.issue_first(dn, nxt.nk);
     };
     if (cur.nk > 0) e.template run<S, true>(acc, dc, cur.nk, s0, stores, dn, chain, at_end);
     else at_end();
     store_wgrad8<F32, TL::TM, TL::TN, TL::WTM, TL::WTN>(p, acc, cur.g, cur.m0, cur.n0, e.wm, e.wn,
                                                    e.lane, scr);
     if (!has_next) break;
-    s0 = chain ? (s0 + cur.nk) & 1 : 0;
+    s0 = chain ? (s0 + cur.nk) & (NS - 1) : 0;
     ready = chain;
     l = ln;
     cur = nxt;
