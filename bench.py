@@ -291,11 +291,12 @@ def router_backward_timing(torch, np, M, Sy, cfg, s, b, X, dev, reps=20):
 # ------------------------------------------------------------------------------------------------
 # forward from x (the skewed full layer, the decode)
 # ------------------------------------------------------------------------------------------------
-def run_forward(torch, np, M, Sy, name, W1, W2, dev, steps, warmup, materialize=False, clock=None):
+def run_forward(torch, np, M, Sy, name, W1, W2, dev, steps, warmup, materialize=False, clock=None,
+                block_m=None):
     """Time the forward from x of workload `name` (router, permutation, gate/up, down, combine).
     W1/W2 are the device weights [G, 2I, H] / [G, H, I] (the workload's own draw). Returns the
-    measurement dict; the useful FLOPs exclude padding rows."""
-    cfg = Sy.get_config(name)
+    measurement dict; the useful FLOPs exclude padding rows. block_m overrides the workload's."""
+    cfg = Sy.get_config(name, **({"block_m": block_m} if block_m else {}))
     T, H, E, K, I, S, B = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.S, cfg.block_m
     x, wg, lb, sb = Sy.draw_x(cfg), Sy.draw_wg(cfg), Sy.draw_logit_bias(cfg), Sy.draw_sel_bias(cfg)
     s = M.make_shape(T, H, E, K, I, S, B)
@@ -589,6 +590,8 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warmup, copy a cold buffer of this many MiB (a plain copy of known "
                          "size that scales the HBM byte counters)")
+    ap.add_argument("--block-m", type=int, default=None,
+                    help="c3/c5: pad the segments to this block size instead of the workload's")
     ap.add_argument("--materialize", action="store_true",
                     help="c3/c5: write x_perm in moe_permute and run grouped_gemm_fwd on it instead "
                          "of gathering x's rows inside the gate/up product")
@@ -630,7 +633,9 @@ def main():
 
     if name in ("c3", "c5"):
         fwd, (x, wg, lb, sb, _) = run_forward(torch, np, M, Sy, name, W1, W2, dev, args.steps,
-                                              args.warmup, args.materialize, clock)
+                                              args.warmup, args.materialize, clock, args.block_m)
+        if args.block_m:
+            cfg = Sy.get_config(name, block_m=args.block_m)
         rows, T = fwd["rows_useful"], cfg.T
         out = {"metric": METRIC, "value": fwd["useful_tflops"], "unit": "TFLOP/s", "n_gpus": 1,
                "steps": args.steps, "warmup": args.warmup, "ms_per_step": fwd["ms"],

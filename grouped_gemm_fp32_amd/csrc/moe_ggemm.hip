@@ -877,11 +877,12 @@ __device__ __forceinline__ void store_tile8(const GemmArgs& p, const f32x16_t (&
 // ------------------------------------------------------------------------------------------------
 // Eight-wavefront engine (two wavefronts per SIMD) for the tall row-grouped tiles: BK = 64, two
 // LDS stages. A stage's DMA (128-byte row segments, the request size the texture path serves
-// best) is spread over the MFMAs of the slices before the stage is needed: the half of it that
-// fits is issued right after the barrier that frees its slot, the rest during the next two
-// slices, so a wavefront held up at DMA issue leaves the matrix unit to the other wavefront of
-// its SIMD, and the last DMA of a stage still has two slices of MFMAs to land. Fragments are
-// read from LDS at the start of each 16-k slice; the other wavefront's MFMAs cover the latency.
+// best) is spread over the MFMAs of the slices before the stage is needed: a third of it is
+// issued right after the barrier that frees its slot, the rest during the next two slices, so a
+// wavefront held up at DMA issue leaves the matrix unit to the other wavefront of its SIMD, and
+// the last DMA of a stage still has two slices of MFMAs to land. Each fragment of the next
+// 16-k slice is read from LDS as soon as the current slice's last MFMA using its registers has
+// issued, so a slice starts with its operands in registers.
 // ------------------------------------------------------------------------------------------------
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile8 {

@@ -4,19 +4,21 @@
 // computed in FP32 and picks the top-6 routed experts per token. Section A2, load-balancing
 // paragraph: a per-expert bias is added to the affinity scores to decide the top-k, and only there.
 //
-// Two kernels:
+// Kernels:
 //   1. router_logits_kernel: logits = x . Wg^T (+ logit_bias) in fp32 on the bf16 matrix unit. x is
 //      bf16, so exact; each fp32 weight is split exactly into three bf16 parts w = hi + mid + lo
 //      (24 significand bits), and three v_mfma_f32_32x32x16_bf16 per k-slice accumulate x*hi +
 //      x*mid + x*lo in fp32. Every product is exact in fp32, so this is the fp32 dot product up
 //      to summation order. One workgroup per 64 tokens (32 for small batches) x 32 experts; its
 //      wavefronts split the 64-k steps and their partial sums are added in wavefront order.
+//      router_logits_dma_kernel computes the same from 16384 tokens on: 64 tokens and every
+//      expert per workgroup, x and Wg staged in LDS by the buffer->LDS DMA.
 //   2. route_kernel, one wavefront per token at a time (a few consecutive tokens each): softmax
 //      over E, key = p + b, K rounds of a wave-wide arg-max on a 64-bit (key, index) code,
-//      weights.
+//      weights. Its cross-lane reductions use DPP and permlane swaps, not the LDS crossbar.
 //   3. count_kernel: per-expert counts of the selected slots, 16 experts x one chunk of topk_idx
-//      per workgroup, summed with one integer atomic per expert and chunk.
-//      The cross-lane reductions use DPP and permlane swaps, not the LDS crossbar.
+//      per workgroup, reduced across the workgroup and added with one integer atomic per expert
+//      and chunk.
 #include "moe_common.h"
 #include "moe_dma.h"
 #include "moe_internal.h"

@@ -108,7 +108,8 @@ size_t moe_workspace_size(const moe_shape_t* shape);
  *                 lower expert index, NaN below every number; slots in rank order
  *   topk_w[T,K] = p_e / sum of the selected p (MOE_NORM_TOPK) or p_e: the bias never enters it
  *   expert_counts[E] = tokens routed to each expert (TR section 6)
- * Modes: x != NULL computes logits into `logits` (one kernel), then routes from them (a second);
+ * Modes: x != NULL computes logits into `logits` (one kernel), then routes from them (a second;
+ * a third counts the routed slots per expert when expert_counts is given);
  * x == NULL reads `logits` as the input; flag MOE_PROBS_IN reads `probs` as the input (x, w_gate,
  * logits unused).
  * Optional (may be NULL): logit_bias, sel_bias (= 0), probs (unless MOE_PROBS_IN), expert_counts.
