@@ -412,6 +412,9 @@ def run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock):
     side_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                for _ in range(args.steps)]
     side_k = [0]
+    # Default: moe_permute writes only the maps and the gate/up product gathers x's rows itself,
+    # writing x_perm (which the gate/up weight gradient reads) from the rows it stages.
+    gather = not args.materialize
 
     def step(ev=None):
         def mark(i):
@@ -421,11 +424,18 @@ def run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock):
         M.moe_route(s, None, None, None, None, LG, b["probs"], b["topk_idx"], b["topk_w"],
                     b["expert_counts"])
         mark(1)
-        M.moe_permute(s, b["topk_idx"], X, b["seg_offsets"], b["tile_group"], b["total_rows"],
-                      b["row_token"], b["pos"], b["x_perm"], b["ws"])
+        M.moe_permute(s, b["topk_idx"], None if gather else X, b["seg_offsets"], b["tile_group"],
+                      b["total_rows"], b["row_token"], b["pos"], None if gather else b["x_perm"],
+                      b["ws"])
         mark(2)
-        M.grouped_gemm_fwd(s, M.MOE_FWD_GATEUP, b["x_perm"], b["seg_offsets"], b["tile_group"],
-                           b["total_rows"], W1, W2, b["h_save"], b["a"], b["y_perm"])
+        if gather:
+            M.grouped_gemm_fwd_gather(s, M.MOE_FWD_GATEUP, X, b["row_token"], b["seg_offsets"],
+                                      b["tile_group"], b["total_rows"], W1, W2, b["h_save"],
+                                      b["a"], b["y_perm"], x_perm=b["x_perm"])
+        else:
+            M.grouped_gemm_fwd(s, M.MOE_FWD_GATEUP, b["x_perm"], b["seg_offsets"],
+                               b["tile_group"], b["total_rows"], W1, W2, b["h_save"], b["a"],
+                               b["y_perm"])
         mark(3)
         M.grouped_gemm_fwd(s, M.MOE_FWD_DOWN, None, b["seg_offsets"], b["tile_group"],
                            b["total_rows"], W1, W2, b["h_save"], b["a"], b["y_perm"])
@@ -512,7 +522,8 @@ def run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock):
         "stages_tflops": {k: round(per_row[k] * rows / (stage_ms[k] * 1e-3) / 1e12, 1)
                           for k in per_row},
         "experts_touched": int(np.sum(counts > 0)) + S,
-        "permutation": "x_perm written by moe_permute",
+        "permutation": ("maps only; the gate/up product gathers x's rows and writes x_perm from "
+                        "its staged rows" if gather else "x_perm written by moe_permute"),
         "streams": ("the unpermute backward on a second stream beside the weight-gradient GEMMs"
                     if side is not None else "one stream"),
     }
@@ -593,8 +604,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=None,
                     help="c3/c5: pad the segments to this block size instead of the workload's")
     ap.add_argument("--materialize", action="store_true",
-                    help="c3/c5: write x_perm in moe_permute and run grouped_gemm_fwd on it instead "
-                         "of gathering x's rows inside the gate/up product")
+                    help="write x_perm in moe_permute and run grouped_gemm_fwd on it instead of "
+                         "gathering x's rows inside the gate/up product (the training step and "
+                         "the c3/c5 forwards)")
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="CPU oracle sample (0 = skip the CPU baseline): for the training workloads "
                          "the token stride (default 8: 1024 tokens, 48 experts x 128 rows, no "

@@ -77,7 +77,7 @@ _SIGS = {
     "moe_permute": (ctypes.c_int, [_SP] + [_P] * 9 + [ctypes.c_size_t, _P]),
     "moe_permute_noalloc": (ctypes.c_int, [_SP] + [_P] * 9),
     "grouped_gemm_fwd": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 10),
-    "grouped_gemm_fwd_gather": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 11),
+    "grouped_gemm_fwd_gather": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 12),
     "grouped_gemm_bwd": (ctypes.c_int, [_SP, ctypes.c_uint32] + [_P] * 14),
     "moe_combine": (ctypes.c_int, [_SP] + [_P] * 6),
     "moe_combine_bwd": (ctypes.c_int, [_SP] + [_P] * 10),
@@ -271,20 +271,20 @@ def grouped_gemm_fwd(shape, which, x_perm, seg_offsets, tile_group, total_rows, 
 
 
 def grouped_gemm_fwd_gather(shape, which, x, row_token, seg_offsets, tile_group, total_rows, w1,
-                            w2, h_save, a, y_perm, stream=None):
+                            w2, h_save, a, y_perm, x_perm=None, stream=None):
     lib = load_library()
     T, H, E, K, I, G, mcap = _dims(shape)
     _need(shape, x=(x, T * H), row_token=(row_token, mcap), seg_offsets=(seg_offsets, G + 1),
           tile_group=(tile_group, mcap // shape.block_m), total_rows=(total_rows, 1),
           w1=(w1, G * 2 * I * H), w2=(w2, G * H * I), h_save=(h_save, mcap * 2 * I),
-          a=(a, mcap * I), y_perm=(y_perm, mcap * H))
+          a=(a, mcap * I), y_perm=(y_perm, mcap * H), x_perm=(x_perm, mcap * H))
     st = _stream(stream, a)
     _check("grouped_gemm_fwd_gather", lib.grouped_gemm_fwd_gather(
         ctypes.byref(shape), which, _ptr(x, "x", _bf16()), _ptr(row_token, "row_token", _i32()),
         _ptr(seg_offsets, "seg_offsets", _i32()), _ptr(tile_group, "tile_group", _i32()),
         _ptr(total_rows, "total_rows", _i32()), _ptr(w1, "w1", _bf16()), _ptr(w2, "w2", _bf16()),
         _ptr(h_save, "h_save", _bf16()), _ptr(a, "a", _bf16()), _ptr(y_perm, "y_perm", _bf16()),
-        st))
+        _ptr(x_perm, "x_perm", _bf16()), st))
 
 
 def grouped_gemm_bwd(shape, which, x_perm, h_save, a, dy_perm, seg_offsets, tile_group, total_rows,

@@ -207,7 +207,7 @@ moe_status_t device_scratch(hipStream_t stream, void** out) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 const char* moe_status_string(int32_t status) {
   switch (status) {
@@ -336,7 +336,7 @@ moe_status_t grouped_gemm_fwd(const moe_shape_t* s, uint32_t which, const uint16
   }
   return hip_status(moe::launch_ggemm_fwd(*s, which, capacity(s), x_perm, nullptr, seg_offsets,
                                           tile_group, total_rows, w1, w2, h_save, a, y_perm,
-                                          (hipStream_t)stream),
+                                          nullptr, (hipStream_t)stream),
                     "grouped_gemm_fwd");
 }
 
@@ -344,7 +344,8 @@ moe_status_t grouped_gemm_fwd_gather(const moe_shape_t* s, uint32_t which, const
                                      const int32_t* row_token, const int32_t* seg_offsets,
                                      const int32_t* tile_group, const int32_t* total_rows,
                                      const uint16_t* w1, const uint16_t* w2, uint16_t* h_save,
-                                     uint16_t* a, uint16_t* y_perm, void* stream) {
+                                     uint16_t* a, uint16_t* y_perm, uint16_t* x_perm,
+                                     void* stream) {
   CHECK_SHAPE(s);
   if (which == 0 || (which & ~(uint32_t)MOE_FWD)) {
     set_err("which must be a non-empty combination of MOE_FWD_GATEUP and MOE_FWD_DOWN");
@@ -369,6 +370,15 @@ moe_status_t grouped_gemm_fwd_gather(const moe_shape_t* s, uint32_t which, const
     REQUIRE_T(x);
     REQUIRE(row_token);
     REQUIRE_T(w1);
+    if (x_perm) {
+      REQUIRE_T(x_perm);
+      const uintptr_t x0 = (uintptr_t)x, x1 = x0 + (uintptr_t)s->T * s->H * 2;
+      const uintptr_t p0 = (uintptr_t)x_perm, p1 = p0 + (uintptr_t)capacity(s) * s->H * 2;
+      if (p0 < x1 && x0 < p1) {
+        set_err("x_perm overlaps x");
+        return MOE_ERR_INVALID_ARG;
+      }
+    }
   }
   if (which & MOE_FWD_DOWN) {
     REQUIRE_T(w2);
@@ -377,7 +387,8 @@ moe_status_t grouped_gemm_fwd_gather(const moe_shape_t* s, uint32_t which, const
   return hip_status(moe::launch_ggemm_fwd(*s, which, capacity(s), x,
                                           (which & MOE_FWD_GATEUP) ? row_token : nullptr,
                                           seg_offsets, tile_group, total_rows, w1, w2, h_save, a,
-                                          y_perm, (hipStream_t)stream),
+                                          y_perm, (which & MOE_FWD_GATEUP) ? x_perm : nullptr,
+                                          (hipStream_t)stream),
                     "grouped_gemm_fwd_gather");
 }
 

@@ -57,6 +57,9 @@ struct GemmArgs {
   int64_t ldo;
   int64_t o_gstride;   // elements per group of the output (wgrad)
   uint16_t* out2;      // h_save written by the forward gate/up epilogue (may be null)
+  // x_perm written by the gathered gate/up product from its staged A rows (may be null): each
+  // column tile's workgroup writes the rows r = nt (mod n_tiles_n) of its row tile
+  uint16_t* out3;
   int M, N, K, I;
   int block_m;
   int max_blk;         // tall tiles: at most this many 128-row blocks per tile (2 or 3)
@@ -958,6 +961,11 @@ struct Eng8 {
   // never waits at a full texture queue.
   static constexpr bool HD = Tr::grouped_rows && !GA;
   uint32_t a_vs, b_vs;
+  // Gathered gate/up with p.out3: per stage each lane of this workgroup copies one 16-byte chunk
+  // of its share of the staged rows (read before the stage's barrier, stored after it, so the
+  // store waits on nothing and no DMA wait waits on it before the next stage's).
+  static constexpr bool CP = GA && Tr::split;
+  int cp_m0 = 0, cp_nt = 0;   // the tile's first row and column-tile index (set per tile)
 
   __device__ __forceinline__ Eng8(const GemmArgs& p_, unsigned char* smem_) : p(p_), smem(smem_) {
     s3 = (lds_u8_t*)smem;
@@ -1248,6 +1256,17 @@ struct Eng8 {
       const int k1 = nx1 ? 0 : kt + 1;
       mma_dma<TL::P1, TL::P2, ACT>(acc, f0, pend, st1, k1, slot ^ 1, f1, slot, 1, true);
       mma_dma<TL::P2, L, ACT>(acc, f1, pend, st1, k1, slot ^ 1, f0, slot, 2, true);
+      uint4 cpv = make_uint4(0, 0, 0, 0);
+      int cp_r = 0;
+      bool cp_on = false;
+      if constexpr (CP) {
+        const int f = wave * 64 + lane;
+        cp_r = cp_nt + (f >> 3) * p.n_tiles_n;
+        cp_on = p.out3 != nullptr && cp_r < BM;
+        if (cp_on)
+          cpv = *reinterpret_cast<const uint4*>(smem + slot * STAGE + cp_r * (BK * 2) +
+                                                (kswz<BK>(cp_r, f & 7) << 4));
+      }
       mma_dma<0, 0, ACT>(acc, f0, false, cu, 0, 0, f1, slot, 3, true);
       if (kt + 1 < nk || chain) {
         // This wave's DMA of stage kt + 1 has landed and its reads of this slot are done; the
@@ -1256,6 +1275,11 @@ struct Eng8 {
         else wait_vm<0>();
         wait_lgkm0();
         block_barrier();
+      }
+      if constexpr (CP) {
+        if (cp_on)
+          *reinterpret_cast<uint4*>(p.out3 + (int64_t)(cp_m0 + cp_r) * p.lda + kt * BK +
+                                    ((wave * 64 + lane) & 7) * 8) = cpv;
       }
       // The next stage's slice 0 is read during this slice in every stage: in the last one the
       // reads find whatever the other slot holds and are never used, but made conditional they
@@ -1283,6 +1307,8 @@ __device__ __forceinline__ void pipe8_tile(const GemmArgs& p, unsigned char* sme
   typedef Eng8<KIND, TL, GA> E;
   E e(p, smem);
   e.set_tile_cols(n0);
+  e.cp_m0 = m0;
+  e.cp_nt = n0 / tile_cols<KIND>(TL::BN);
   typename E::Dma st;
   e.setup(st, g, m0, n0, kbeg, klen);
   typename E::Acc acc;
@@ -1566,8 +1592,12 @@ int tall_max_blk(int64_t rows, int G, int n_tiles_n) {
 
 // Row-grouped kinds: tall tiles for block_m % 128 == 0, 64-row tiles for block_m == 64, the
 // register-staged engine for 16 and 32.
+// *rows_copied (if given) tells whether the launch writes a.out3 (the gathered gate/up product
+// on tall tiles, where each row tile has enough column tiles to share out its rows).
 template <int KIND>
-hipError_t launch_rows(GemmArgs a, int64_t mcap, int64_t rows, hipStream_t st) {
+hipError_t launch_rows(GemmArgs a, int64_t mcap, int64_t rows, hipStream_t st,
+                       bool* rows_copied = nullptr) {
+  if (rows_copied) *rows_copied = false;
   if (a.block_m % kTallBlk == 0) {
     if (a.seg == nullptr) return hipErrorInvalidValue;
     constexpr int cols = tile_cols<KIND>(kTall8BN);
@@ -1578,6 +1608,10 @@ hipError_t launch_rows(GemmArgs a, int64_t mcap, int64_t rows, hipStream_t st) {
     const int64_t grid = (tiles * a.n_tiles_n + kNumXcd - 1) / kNumXcd * kNumXcd;
     if constexpr (KIND == kFwdGateUp) {
       if (a.a_rows) {
+        // each of a row tile's n_tiles_n workgroups copies every n_tiles_n-th row of its stages,
+        // at most 64 rows a stage (8 lanes of 16 bytes per 128-byte row stage)
+        if (a.out3 && a.n_tiles_n * 64 < a.max_blk * kTallBlk) a.out3 = nullptr;
+        if (rows_copied) *rows_copied = a.out3 != nullptr;
         hipLaunchKernelGGL((ggemm_tall8_kernel<KIND, true>), dim3((unsigned)grid), dim3(kThreads8),
                            0, st, a);
         return hipGetLastError();
@@ -1612,7 +1646,8 @@ hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
                             const uint16_t* x_perm, const int32_t* row_token,
                             const int32_t* seg_offsets, const int32_t* tile_group,
                             const int32_t* total_rows, const uint16_t* w1, const uint16_t* w2,
-                            uint16_t* h_save, uint16_t* a, uint16_t* y_perm, hipStream_t st) {
+                            uint16_t* h_save, uint16_t* a, uint16_t* y_perm, uint16_t* x_perm_out,
+                            hipStream_t st) {
   GemmArgs g{};
   g.block_m = s.block_m;
   g.I = s.I;
@@ -1628,15 +1663,21 @@ hipError_t launch_ggemm_fwd(const moe_shape_t& s, uint32_t which, int64_t mcap,
   g.a_bytes = row_token ? (int64_t)s.T * s.H * 2 : 0;
   g.b = w1; g.ldb = s.H; g.b_gstride = (int64_t)2 * s.I * s.H;
   g.out = a; g.ldo = s.I; g.out2 = h_save;
+  g.out3 = row_token ? x_perm_out : nullptr;
   g.N = s.I; g.K = s.H;
   if (which & MOE_FWD_GATEUP) {
-    hipError_t e = launch_rows<kFwdGateUp>(g, mcap, rows, st);
+    bool copied = false;
+    hipError_t e = launch_rows<kFwdGateUp>(g, mcap, rows, st, &copied);
     if (e != hipSuccess) return e;
+    if (g.out3 && !copied) {   // the launch could not write x_perm from its stages
+      e = launch_gather_rows(s, mcap, total_rows, row_token, x_perm, x_perm_out, st);
+      if (e != hipSuccess) return e;
+    }
   }
   if (!(which & MOE_FWD_DOWN)) return hipSuccess;
   // down
   g.a = a; g.lda = s.I;
-  g.a_rows = nullptr; g.a_bytes = 0;
+  g.a_rows = nullptr; g.a_bytes = 0; g.out3 = nullptr;
   g.b = w2; g.ldb = s.I; g.b_gstride = (int64_t)s.H * s.I;
   g.out = y_perm; g.ldo = s.H; g.out2 = nullptr;
   g.N = s.H; g.K = s.I;

@@ -248,11 +248,16 @@ hipError_t launch_permute(const moe_shape_t& s, int64_t mcap, const int32_t* top
                      dim3(kThreads), 0, st, mcap, total_rows, row_token);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(nblk), dim3(kThreads), sc_lds, st, s.T, s.K, s.E,
                      s.S, TB, topk_idx, ws, seg_offsets, pos, row_token);
-  if (x) {
-    const int64_t rows_per_wg = kThreads / 64;
-    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((mcap + rows_per_wg - 1) / rows_per_wg)),
-                       dim3(kThreads), 0, st, s.T, s.H, mcap, total_rows, row_token, x, x_perm);
-  }
+  if (x) return launch_gather_rows(s, mcap, total_rows, row_token, x, x_perm, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const moe_shape_t& s, int64_t mcap, const int32_t* total_rows,
+                              const int32_t* row_token, const uint16_t* x, uint16_t* x_perm,
+                              hipStream_t st) {
+  const int64_t rows_per_wg = kThreads / 64;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((mcap + rows_per_wg - 1) / rows_per_wg)),
+                     dim3(kThreads), 0, st, s.T, s.H, mcap, total_rows, row_token, x, x_perm);
   return hipGetLastError();
 }
 

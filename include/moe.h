@@ -183,16 +183,22 @@ moe_status_t grouped_gemm_fwd(const moe_shape_t* shape, uint32_t which, const ui
  * with x == NULL and no x_perm buffer exists. row_token [Mcap] and the segments come from that
  * moe_permute call. Every output equals grouped_gemm_fwd's on the x_perm moe_permute would have
  * written, bit for bit (same operands, same arithmetic).
- * For inference: the weight gradient of the gate/up projection (grouped_gemm_bwd) still reads an
- * x_perm. x [T,H] bf16, 16-byte aligned; needs T*H*2 <= 2^31 bytes (else MOE_ERR_UNSUPPORTED).
- * Other arguments, layouts and errors as grouped_gemm_fwd; x and row_token are unused (may be
- * NULL) for MOE_FWD_DOWN alone.
+ * x_perm [Mcap,H] bf16 (optional, may be NULL; 16-byte aligned, must not overlap x): the weight
+ * gradient of the gate/up projection (grouped_gemm_bwd) reads the permuted rows, so a training
+ * step passes x_perm here and gets for rows r < total_rows exactly what moe_permute would have
+ * written (x[row_token[r]], zero on padding rows; rows >= total_rows untouched). On tall tiles
+ * (block_m a multiple of 128) the gate/up product writes it from the rows it has staged for its
+ * own use, so x is read once; otherwise a separate row copy runs on the same stream.
+ * x [T,H] bf16, 16-byte aligned; needs T*H*2 <= 2^31 bytes (else MOE_ERR_UNSUPPORTED).
+ * Other arguments, layouts and errors as grouped_gemm_fwd; x, row_token and x_perm are unused
+ * (may be NULL) for MOE_FWD_DOWN alone.
  */
 moe_status_t grouped_gemm_fwd_gather(const moe_shape_t* shape, uint32_t which, const uint16_t* x,
                                      const int32_t* row_token, const int32_t* seg_offsets,
                                      const int32_t* tile_group, const int32_t* total_rows,
                                      const uint16_t* w1, const uint16_t* w2, uint16_t* h_save,
-                                     uint16_t* a, uint16_t* y_perm, void* stream);
+                                     uint16_t* a, uint16_t* y_perm, uint16_t* x_perm,
+                                     void* stream);
 
 /*
  * grouped_gemm_bwd — gradients of the grouped expert FFN with the routing held fixed.

@@ -263,35 +263,48 @@ def test_binding_checks_tensor_sizes_against_the_shape(lib):
 
 
 def test_gather_forward_checks(lib):
-    """grouped_gemm_fwd_gather: x and row_token replace x_perm for the gate/up product."""
+    """grouped_gemm_fwd_gather: x and row_token replace x_perm for the gate/up product, and an
+    optional x_perm output receives the permuted rows."""
     s = M.make_shape(8, 256, 8, 2, 128, 1, 16)
     d, odd = ctypes.c_void_p(16), ctypes.c_void_p(24)
     full = [d] * 10   # x, row_token, seg_offsets, tile_group, total_rows, w1, w2, h_save, a, y_perm
-    assert lib.grouped_gemm_fwd_gather(ctypes.byref(s), 0, *full, None) == -1
-    assert lib.grouped_gemm_fwd_gather(ctypes.byref(s), 4, *full, None) == -1
+
+    def call(shape, which, args, x_perm=None):
+        return lib.grouped_gemm_fwd_gather(ctypes.byref(shape), which, *args, x_perm, None)
+
+    assert call(s, 0, full) == -1
+    assert call(s, 4, full) == -1
     for i in range(10):
         if i == 7:        # h_save is optional
             continue
         a = list(full)
         a[i] = None
-        assert lib.grouped_gemm_fwd_gather(ctypes.byref(s), M.MOE_FWD, *a, None) == -1, i
+        assert call(s, M.MOE_FWD, a) == -1, i
         assert "NULL" in M.moe_last_error()
     for i in (0, 5, 6, 7, 8, 9):   # bf16 tensors: x, w1, w2, h_save, a, y_perm
         a = list(full)
         a[i] = odd
-        assert lib.grouped_gemm_fwd_gather(ctypes.byref(s), M.MOE_FWD, *a, None) == -1, i
+        assert call(s, M.MOE_FWD, a) == -1, i
         assert "aligned" in M.moe_last_error()
-    # the down product alone reads neither x nor row_token
+    # the optional x_perm output: 16-byte aligned and apart from x ([T,H] against [Mcap,H])
+    assert call(s, M.MOE_FWD, full, x_perm=odd) == -1
+    assert "aligned" in M.moe_last_error()
+    x0 = 1 << 24
+    with_x = [ctypes.c_void_p(x0)] + full[1:]
+    for xp in (x0, x0 + 8 * 256 * 2 - 16, x0 - M.moe_row_capacity(s) * 256 * 2 + 16):
+        assert call(s, M.MOE_FWD, with_x, x_perm=ctypes.c_void_p(xp)) == -1, xp
+        assert "overlaps" in M.moe_last_error()
+    # the down product alone reads neither x nor row_token, and writes no x_perm
     a = list(full)
     a[0] = a[1] = None
     st = M.make_shape(0, 256, 8, 2, 128, 1, 16)
-    assert lib.grouped_gemm_fwd_gather(ctypes.byref(st), M.MOE_FWD_DOWN, *a, None) == 0
+    assert call(st, M.MOE_FWD_DOWN, a, x_perm=odd) == 0
     # x addressed with 32-bit byte offsets: T*H*2 <= 2^31
     big = M.make_shape(262144, 8192, 8, 2, 128, 1, 128)
-    assert lib.grouped_gemm_fwd_gather(ctypes.byref(big), M.MOE_FWD, *full, None) == -2
+    assert call(big, M.MOE_FWD, full) == -2
     assert "2^31" in M.moe_last_error()
     empty = M.make_shape(0, 256, 8, 2, 128, 1, 16)
-    assert lib.grouped_gemm_fwd_gather(ctypes.byref(empty), M.MOE_FWD, *([None] * 10), None) == 0
+    assert call(empty, M.MOE_FWD, [None] * 10) == 0
 
 
 def test_gemm_32bit_span_limits(lib):
@@ -304,7 +317,7 @@ def test_gemm_32bit_span_limits(lib):
         return lib.grouped_gemm_fwd(ctypes.byref(s), M.MOE_FWD, *([d] * 9), None)
 
     def gather(s):
-        return lib.grouped_gemm_fwd_gather(ctypes.byref(s), M.MOE_FWD, *([d] * 10), None)
+        return lib.grouped_gemm_fwd_gather(ctypes.byref(s), M.MOE_FWD, *([d] * 11), None)
 
     def bwd(s, which):
         return lib.grouped_gemm_bwd(ctypes.byref(s), which, *([d] * 13), None)
