@@ -18,7 +18,8 @@
 //      weights. Its cross-lane reductions use DPP and permlane swaps, not the LDS crossbar.
 //   3. count_kernel: per-expert counts of the selected slots, 16 experts x one chunk of topk_idx
 //      per workgroup, reduced across the workgroup and added with one integer atomic per expert
-//      and chunk.
+//      and chunk (into counts cleared first); a batch of one chunk (decode) stores its sums
+//      directly, with no clear.
 #include "moe_common.h"
 #include "moe_dma.h"
 #include "moe_internal.h"
@@ -443,6 +444,9 @@ constexpr int kCntThreads = 256;
 constexpr int kCntPer = 8;                                      // entries per lane
 constexpr int64_t kCntChunk = (int64_t)kCntThreads * kCntPer;   // entries per workgroup
 
+// STORE: a single chunk (one workgroup row): its sums are the counts, stored without a prior
+// clear; otherwise each chunk adds its sums to counts, which must start at zero.
+template <bool STORE>
 __global__ __launch_bounds__(kCntThreads) void count_kernel(int64_t n, int E,
                                                             const int32_t* __restrict__ idx,
                                                             int32_t* __restrict__ counts) {
@@ -480,7 +484,8 @@ __global__ __launch_bounds__(kCntThreads) void count_kernel(int64_t n, int E,
     int x = 0;
 #pragma unroll
     for (int w = 0; w < kCntThreads / 64; ++w) x += part[w][threadIdx.x];
-    if (x) atomicAdd(&counts[e0 + threadIdx.x], x);
+    if constexpr (STORE) counts[e0 + threadIdx.x] = x;
+    else if (x) atomicAdd(&counts[e0 + threadIdx.x], x);
   }
 }
 
@@ -499,7 +504,10 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t st) {
 }
 
 namespace {
-// counts were cleared before the routing kernels ran (fill_i32_kernel)
+// One chunk of routed slots (decode-sized batches) is counted and stored by one row of
+// workgroups; more are added up, into counts cleared before the routing kernels ran.
+bool counts_single_chunk(const moe_shape_t& s) { return (int64_t)s.T * s.K <= kCntChunk; }
+
 hipError_t launch_counts(const moe_shape_t& s, const int32_t* topk_idx, int32_t* counts,
                          hipStream_t st) {
   hipError_t e = hipGetLastError();
@@ -507,7 +515,10 @@ hipError_t launch_counts(const moe_shape_t& s, const int32_t* topk_idx, int32_t*
   const int64_t n = (int64_t)s.T * s.K;
   const dim3 grid((unsigned)((s.E + kCntExperts - 1) / kCntExperts),
                   (unsigned)((n + kCntChunk - 1) / kCntChunk));
-  hipLaunchKernelGGL(count_kernel, grid, dim3(kCntThreads), 0, st, n, s.E, topk_idx, counts);
+  if (counts_single_chunk(s))
+    hipLaunchKernelGGL(count_kernel<true>, grid, dim3(kCntThreads), 0, st, n, s.E, topk_idx, counts);
+  else
+    hipLaunchKernelGGL(count_kernel<false>, grid, dim3(kCntThreads), 0, st, n, s.E, topk_idx, counts);
   return hipGetLastError();
 }
 }  // namespace
@@ -516,7 +527,7 @@ hipError_t launch_route(const moe_shape_t& s, const uint16_t* x, const float* wg
                         const float* logit_bias, const float* sel_bias, float* logits,
                         float* probs, int32_t* topk_idx, float* topk_w, int32_t* counts,
                         hipStream_t st) {
-  if (counts) {
+  if (counts && !counts_single_chunk(s)) {
     hipError_t e = launch_fill_i32(counts, 0, s.E, st);
     if (e != hipSuccess) return e;
   }
