@@ -21,6 +21,9 @@
 //   DgradGateUp dx_perm = dh . W1[g]
 //   WgradDown   dW2[g] = dy_perm_seg^T . a_seg        (contraction over the segment's rows)
 //   WgradGateUp dW1[g] = dh_seg^T . x_perm_seg
+// FwdGateUp can also gather its rows from x through the permutation map (row r = x[row_token[r]],
+// zero on padding rows) and, on tall tiles, write x_perm from the rows it stages, so the training
+// step's permutation copies nothing.
 #include <type_traits>
 
 #include "moe_common.h"
