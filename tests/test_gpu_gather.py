@@ -108,11 +108,12 @@ def test_gather_forward_full_size(name):
     _bitexact(ref, got)
 
 
-def test_gather_forward_tile_heights():
-    """12 blocks of 128 rows per expert over eight 128-column tiles: the tall tiles come out 384
-    rows high (and the x_perm copy shares out 48 rows per workgroup and stage). Bit for bit
-    against the materialised path."""
-    T, H, E, K, I, S, B = 6144, 256, 8, 2, 1024, 0, 128
+@pytest.mark.parametrize("I", [1024, 768])
+def test_gather_forward_tile_heights(I):
+    """12 blocks of 128 rows per expert: the tall tiles come out 384 rows high. Over eight
+    128-column tiles the x_perm copy shares out 48 rows per workgroup and stage; over six, 64 (all
+    512 lanes of each workgroup, the most it takes). Bit for bit against the materialised path."""
+    T, H, E, K, S, B = 6144, 256, 8, 2, 0, 128
     cfg = get_config("c1", T=T, H=H, E=E, K=K, I=I, S=S, block_m=B, seed=9)
     idx = np.stack([(np.arange(T) + j) % E for j in range(K)], axis=1).astype(np.int32)
     log(f"gather fwd tile heights T={T} E={E} I={I}")
