@@ -67,6 +67,7 @@ PART_OF = {
     "router_logits_kernel<1,8>": "route (router logits)",
     "router_logits_dma_kernel<1>": "route (router logits)", "router_logits_dma_kernel<2>": "route (router logits)",
     "fill_i32_kernel": "route (count clear)", "count_kernel": "route (expert counts)",
+    "count_kernel<false>": "route (expert counts)", "count_kernel<true>": "route (expert counts)",
     "perm_clear_rows_kernel": "permute (maps)",
     "perm_hist_kernel": "permute (segments)", "perm_segment_kernel": "permute (segments)",
     "perm_scatter_kernel": "permute (maps)", "zero_pad_rows_kernel": "combine_bwd (padding rows)",
