@@ -957,12 +957,13 @@ struct Eng8 {
     v4u32_t ra, rb;
     uint32_t a_off0, b_off0;
     uint32_t a_offs[GA ? TL::LA : 1];   // gathered A: one lane offset per DMA instruction
+    uint32_t a_offs_hi[GA ? TL::LA : 1];   // ... and for the rows of the wave 4 above (HD)
   };
   uint32_t a_kstep, b_kstep;
   // HD: only waves 0-3 (one per SIMD) issue the DMA, each its own instructions and those of the
   // wave 4 above it (rows 32 further on, LDS 4 KiB further on), so the other wave of each SIMD
-  // never waits at a full texture queue.
-  static constexpr bool HD = Tr::grouped_rows && !GA;
+  // never waits at a full texture queue. Gathered rows: waves 0-3 hold the lane offsets of both.
+  static constexpr bool HD = Tr::grouped_rows;
   uint32_t a_vs, b_vs;
   // Gathered gate/up with p.out3: per stage each lane of this workgroup copies one 16-byte chunk
   // of its share of the staged rows (read before the stage's barrier, stored after it, so the
@@ -1000,6 +1001,10 @@ struct Eng8 {
         const int tok = p.a_rows[m0 + r];
         st.a_offs[i] = tok >= 0
             ? (uint32_t)(((int64_t)tok * p.lda + kswz<BK>(r, lane % CPR) * 8) * 2) : kPastEnd;
+        const int r2 = r + 4 * RPI;
+        const int tok2 = wave < 4 ? p.a_rows[m0 + r2] : -1;
+        st.a_offs_hi[i] = tok2 >= 0
+            ? (uint32_t)(((int64_t)tok2 * p.lda + kswz<BK>(r2, lane % CPR) * 8) * 2) : kPastEnd;
       }
       st.a_off0 = 0;
     } else if constexpr (!AMN) {
@@ -1050,7 +1055,7 @@ struct Eng8 {
               sl + A_BYTES + (d * NW + wave) * 1024);
     } else {
       const int i = d - LB;
-      if constexpr (GA) dma16(st.ra, st.a_offs[i] + uniform(kt * a_kstep), sl + (i * NW + wave) * 1024);
+      if constexpr (GA) dma16(st.ra, (hv ? st.a_offs_hi[i] : st.a_offs[i]) + uniform(kt * a_kstep), sl + (i * NW + wave) * 1024);
       else dma16(st.ra, st.a_off0 + uniform(kt * a_kstep + a_istride(i) + hv * a_vs), sl + (i * NW + wave) * 1024);
     }
   }
