@@ -966,10 +966,10 @@ struct Eng8 {
   uint32_t a_kstep, b_kstep;
   // HD: only waves 0-3 (one per SIMD) issue the DMA, each its own instructions and those of the
   // wave 4 above it (LDS 4 KiB further on; K-major operands 32 rows further on, MN-major ones
-  // 256 chunks, a whole number of k-rows), so the other wave of each SIMD never waits at a full texture queue. Gathered rows:
-  // waves 0-3 hold the lane offsets of both. The down weight gradient keeps every wave issuing
-  // its own share (about 2% faster there; the gate/up one gains about 1% from HD).
-  static constexpr bool HD = Tr::grouped_rows || KIND == kWgradGateUp;
+  // 256 chunks, a whole number of k-rows), so the other wave of each SIMD never waits at a full
+  // texture queue. Gathered rows: waves 0-3 hold the lane offsets of both. (false: every wave
+  // issues its own share.)
+  static constexpr bool HD = true;
   uint32_t a_vs, b_vs;
   // Gathered gate/up with p.out3: per stage each lane of this workgroup copies one 16-byte chunk
   // of its share of the staged rows (read before the stage's barrier, stored after it, so the
@@ -1425,15 +1425,10 @@ __global__ __launch_bounds__(kThreads, 1) void ggemm_block64_kernel(GemmArgs p) 
 // fixed costs (first DMA, 128 KiB of stores) are as large as its MFMAs: the kernel is persistent,
 // one workgroup per CU walking its XCD's tiles, and it issues the next tile's first two stages
 // before storing the current tile, so the stores drain under the next tile's MFMAs.
-typedef Tile8<256, 256, 4, 2> Wgrad8Tile;
-// The tile per kind differs only in when a stage's DMA goes out: the gate/up kind, whose waves 0-3
-// issue all of it, puts it all out in the slice right after the freeing barrier; the down kind
-// spreads it over that slice and the next two (measured: 2-3% and about 0.7% faster than a third
-// per slice).
-template <int KIND> struct Wgrad8Kind {
-  static constexpr bool all_first = KIND == kWgradGateUp;
-  typedef Tile8<256, 256, 4, 2, all_first ? 12 : 6, all_first ? 12 : 10> type;
-};
+// A stage's whole DMA (issued by waves 0-3) goes out in the slice right after the freeing barrier:
+// with the stores of the previous tile in the same queues, the earliest start pays (2-4% against
+// a third per slice).
+typedef Tile8<256, 256, 4, 2, 12, 12> Wgrad8Tile;
 constexpr int kStoreNT = 2;   // cache-policy operand of buffer stores: non-temporal
 constexpr int kWgradScr = 4096;                     // epilogue staging per wavefront
 // Stores per wavefront per tile: bf16 dW in 32 x 64 passes (4 stores each); fp32 dW in 32 x 32
@@ -1503,9 +1498,7 @@ __device__ __forceinline__ int ld_scalar(const int32_t* a, int64_t i) {
 template <int KIND, bool F32>
 __global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
-  typedef typename Wgrad8Kind<KIND>::type TL;
-  static_assert(TL::TM == Wgrad8Tile::TM && TL::TN == Wgrad8Tile::TN && TL::L == Wgrad8Tile::L,
-                "same tile as the launch and the store count assume");
+  typedef Wgrad8Tile TL;
   typedef Eng8<KIND, TL> E;
   constexpr int S = wgrad_stores<F32>(), L = TL::L;
   const int64_t per_g = (int64_t)p.n_tiles_m * p.n_tiles_n, total = per_g * p.G;
