@@ -1387,11 +1387,19 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   }
   __syncthreads();
   const int64_t n_tiles = pref[G];
-  const int64_t L = xcd_remap(blockIdx.x, n_tiles * p.n_tiles_n);
+  // Row tiles are dealt to the XCDs in turn (hardware places workgroup b on XCD b % 8): XCD x
+  // takes row tiles x, x + 8, x + 16, ..., each with all its column tiles in a row, so the tiles
+  // that share a row tile's activation panel share that XCD's L2. Dealt in turn rather than in
+  // contiguous ranges, every XCD gets its share of the tall and the short tiles: with skewed
+  // routing the segments shrink along the group order, and equal-length ranges would give one
+  // XCD the many one-block tiles of the rare experts and another the three-block tiles of the
+  // popular ones.
+  const int64_t k = blockIdx.x / kNumXcd;
+  const int64_t L = (int64_t)(blockIdx.x % kNumXcd) + kNumXcd * (k / p.n_tiles_n);
   int g = 0, ti = 0, nt = 0;
-  if (L >= 0) {
-    ti = (int)(L / p.n_tiles_n);
-    nt = (int)(L % p.n_tiles_n);
+  if (L < n_tiles) {
+    ti = (int)L;
+    nt = (int)(k % p.n_tiles_n);
     int lo = 0, hi = G - 1;   // group of tile ti: largest g with pref[g] <= ti
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -1401,7 +1409,7 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   }
   const int t0 = pref[g], ntg = pref[g + 1] - t0;
   __syncthreads();   // pref is dead from here on: the DMA ring may overwrite it
-  if (L < 0) return;
+  if (L >= n_tiles) return;
   const int nb = (p.seg[g + 1] - p.seg[g]) / kTallBlk;
   const int local = ti - t0, base = nb / ntg, extra = nb % ntg;
   const int blk0 = local * base + min(local, extra), nblk = base + (local < extra ? 1 : 0);
@@ -1634,7 +1642,8 @@ hipError_t launch_rows(GemmArgs a, int64_t mcap, int64_t rows, hipStream_t st,
     a.max_blk = tall_max_blk(rows, a.G, a.n_tiles_n);
     // sum over groups of ceil(nb_g / mb) <= (sum nb_g + (mb - 1) G) / mb, sum nb_g <= mcap / 128
     const int64_t tiles = (mcap / kTallBlk + (a.max_blk - 1) * (int64_t)a.G) / a.max_blk + 1;
-    const int64_t grid = (tiles * a.n_tiles_n + kNumXcd - 1) / kNumXcd * kNumXcd;
+    // every XCD gets ceil(tiles / 8) row tiles' worth of workgroups (see the kernel's mapping)
+    const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * a.n_tiles_n * kNumXcd;
     if constexpr (KIND == kFwdGateUp) {
       if (a.a_rows) {
         // each of a row tile's n_tiles_n workgroups copies every n_tiles_n-th row of its stages,
