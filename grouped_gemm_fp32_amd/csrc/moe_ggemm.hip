@@ -1445,6 +1445,23 @@ __global__ __launch_bounds__(kThreads, 1) void ggemm_block64_kernel(GemmArgs p) 
 typedef Tile8<256, 256, 4, 2, 12, 12> Wgrad8Tile;
 constexpr int kStoreNT = 2;   // cache-policy operand of buffer stores: non-temporal
 constexpr int kWgradScr = 4096;                     // epilogue staging per wavefront
+// A weight-gradient tile's fixed cost in stage times (first DMA latency, 128 KiB of stores): at
+// the benchmark shape tiles of 6 stages take about 16 us and tiles of 48 stages about 95 us.
+constexpr int kWgradTileFixed = 3;
+
+// Sum and inclusive prefix sum of an int64 over the 64 lanes of a wavefront.
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
+  return __shfl(wave_incl_scan_i64(x), 63, 64);
+}
 // Stores per wavefront per tile: bf16 dW in 32 x 64 passes (4 stores each); fp32 dW in 32 x 32
 // passes (4 stores each, twice as many passes).
 template <bool F32> constexpr int wgrad_stores() {
@@ -1516,10 +1533,43 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_wgrad8_kernel(GemmArgs p) 
   typedef Eng8<KIND, TL> E;
   constexpr int S = wgrad_stores<F32>(), L = TL::L;
   const int64_t per_g = (int64_t)p.n_tiles_m * p.n_tiles_n, total = per_g * p.G;
-  const int64_t per_x = (total + kNumXcd - 1) / kNumXcd;   // each XCD walks a contiguous range
   const int xcd = blockIdx.x % kNumXcd, nwg = gridDim.x / kNumXcd;
-  const int64_t lend = min((int64_t)(xcd + 1) * per_x, total);
-  int64_t l = (int64_t)xcd * per_x + blockIdx.x / kNumXcd;
+  // Each XCD walks a contiguous range of tiles (groups in order, so tiles that share operand
+  // panels share its L2), cut so that every XCD gets an eighth of the estimated work: a tile of a
+  // segment with nk stages costs nk + kWgradTileFixed stage times (its first DMA and its stores).
+  // With skewed routing equal tile counts would leave most of the work to the XCDs that hold the
+  // popular experts.
+  int64_t lbeg, lend;
+  {
+    int64_t* sb = reinterpret_cast<int64_t*>(smem);   // [2]; the DMA ring takes the LDS afterwards
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      auto tile_cost = [&](int g) -> int64_t {
+        if (g >= p.G) return 0;
+        const int klen = ld_scalar(p.seg, g + 1) - ld_scalar(p.seg, g);
+        return (klen + TL::BK - 1) / TL::BK + kWgradTileFixed;
+      };
+      int64_t all = 0;
+      for (int base = 0; base < p.G; base += 64) all += wave_sum_i64(per_g * tile_cost(base + lane));
+      const int64_t thr0 = all * xcd / kNumXcd, thr1 = all * (xcd + 1) / kNumXcd;
+      // the first tile whose preceding work reaches thr, inside the group that spans thr
+      int64_t run = 0;
+      for (int base = 0; base < p.G; base += 64) {
+        const int g = base + lane;
+        const int64_t tc = tile_cost(g), c = per_g * tc;
+        const int64_t incl = wave_incl_scan_i64(c), pre = run + incl - c;
+        if (c > 0 && pre <= thr0 && thr0 < pre + c) sb[0] = g * per_g + (thr0 - pre + tc - 1) / tc;
+        if (c > 0 && pre <= thr1 && thr1 < pre + c) sb[1] = g * per_g + (thr1 - pre + tc - 1) / tc;
+        run += __shfl(incl, 63, 64);
+      }
+      if (lane == 0 && thr1 >= all) sb[1] = total;   // the last XCD's range ends with the tiles
+    }
+    __syncthreads();
+    lbeg = sb[0];
+    lend = sb[1];
+    __syncthreads();
+  }
+  int64_t l = lbeg + blockIdx.x / kNumXcd;
   if (l >= lend) return;
   struct T { int g, m0, n0, kbeg, klen, nk; };
   const bool m_fast = p.M <= p.N;
