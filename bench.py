@@ -21,7 +21,9 @@ stream as a fraction of HBM bandwidth). Both gather x's rows inside the gate/up 
 Other workloads: `--workload c3` / `c5` make those forwards the main line; `--workload dense`
 runs the default step on a dense SwiGLU FFN expressed as one group (E = K = 1, intermediate
 11264); `--workload ep8` runs it on one GPU's share of the default layer under 8-way expert
-parallelism: 16 local experts with 3072 rows each (the exchange between GPUs is not part of it).
+parallelism: 16 local experts with 3072 rows each (the exchange between GPUs is not part of it);
+`--workload c4z` runs the default step with Zipf(1.1)-skewed routing (segments from 0 to several
+thousand rows).
 
 Prints one JSON line. `value` is the useful grouped-GEMM TFLOP/s of the whole step (padding
 excluded). It also carries the dominant kernel's roofline, timed with HIP events on the launch
@@ -58,6 +60,8 @@ DESC = {
     "c3": "MoE FFN full layer forward from x, skewed routing (T=16384, hidden=4096, 128 "
           "experts top-6 with Zipf(1.1) logit offsets + 2 shared experts, intermediate=1408, "
           "block_m=128)",
+    "c4z": "grouped-GEMM MoE FFN forward+backward, Zipf(1.1)-skewed routing (T=8192, "
+           "hidden=4096, 128 experts top-6, intermediate=1408, block_m=128)",
     "c5": "MoE FFN decode forward from x, random routing (T=256, hidden=4096, 128 experts "
           "top-6 + 2 shared experts, intermediate=1408, block_m=16)",
 }
@@ -397,7 +401,8 @@ def run_forward(torch, np, M, Sy, name, W1, W2, dev, steps, warmup, materialize=
 def run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock):
     cfg = Sy.get_config(name)
     T, H, E, K, I, S, B = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.S, cfg.block_m
-    dy, logits = Sy.draw_dy(cfg), Sy.uniform_logits(cfg)
+    dy = Sy.draw_dy(cfg)
+    logits = Sy.skewed_logits(cfg) if cfg.routing == "zipf" else Sy.uniform_logits(cfg)
     s = M.make_shape(T, H, E, K, I, S, B)
     b = M.alloc_buffers(s, dev, backward=True, save_h=True)
     X = _bf(np, torch, x, dev)
@@ -485,7 +490,8 @@ def run_train_step(torch, np, M, Sy, name, x, w1, w2, W1, W2, dev, args, clock):
     step()
     torch.cuda.synchronize()
     counts = b["expert_counts"].cpu().numpy()
-    assert np.all(counts == T * K // E), "uniform routing not reproduced"
+    if cfg.routing != "zipf":
+        assert np.all(counts == T * K // E), "uniform routing not reproduced"
     ms_step, st_ms = _time_steps(torch, np, step, len(stages), args.steps, args.warmup)
     stage_ms = dict(zip(stages, st_ms))
     if side is not None:   # on its own stream, beside the weight-gradient GEMMs
@@ -585,12 +591,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("c2", "c3", "c5", "dense", "ep8"), default="c2",
+    ap.add_argument("--workload", choices=("c2", "c3", "c5", "dense", "ep8", "c4z"), default="c2",
                     help="c2: forward+backward at the uniform 8192-token shape (default; the line "
                          "also carries the c3 and c5 forwards); c3: skewed 16384-token full layer "
                          "forward; c5: 256-token decode forward; dense: forward+backward of a dense "
                          "SwiGLU FFN (intermediate 11264) as one group; ep8: forward+backward of one "
-                         "GPU's 16-expert share under 8-way expert parallelism (3072 rows per expert)")
+                         "GPU's 16-expert share under 8-way expert parallelism (3072 rows per expert); "
+                         "c4z: the default forward+backward with Zipf(1.1)-skewed routing")
     ap.add_argument("--serial", action="store_true",
                     help="training step: run the unpermute backward after the weight gradients on "
                          "the one stream instead of beside them on a second stream")
@@ -682,7 +689,8 @@ def main():
         out["decode_c5"], _ = run_forward(torch, np, M, Sy, "c5", W15, W25, dev,
                                           max(args.forward_steps, 20), 5, args.materialize, clock)
         del W15, W25
-    stride = args.cpu_sample if args.cpu_sample is not None else 8
+    # The sample is padding-free only under uniform routing; the skewed step skips it by default.
+    stride = args.cpu_sample if args.cpu_sample is not None else (0 if name == "c4z" else 8)
     if stride > 0:
         log(f"[bench] CPU oracle on one token in {stride}")
         G = cfg.E + cfg.S

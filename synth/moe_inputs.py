@@ -24,7 +24,7 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32",
     "draw_x", "draw_wg", "draw_sel_bias", "draw_logit_bias", "draw_w1", "draw_w2",
     "draw_w1_all", "draw_w2_all", "draw_dy", "draw_topk_given", "draw_probs", "draw_logits",
-    "uniform_topk", "uniform_logits", "num_groups",
+    "uniform_topk", "uniform_logits", "skewed_logits", "num_groups",
 ]
 
 # Stream tags: one per tensor kind.
@@ -82,6 +82,10 @@ CONFIGS = {
     # over the 16 experts (the GEMMs see exactly that shape; the exchange itself is not modelled).
     "ep8": MoEConfig("ep8", T=8192, H=4096, E=16, K=6, I=1408, S=0, block_m=128, seed=0,
                      routing="uniform"),
+    # The c4 training step with Zipf(1.1)-skewed routing (a router early in training, before the
+    # bias balances the load): expert popularity ~ rank^-1.1, K distinct experts per token.
+    "c4z": MoEConfig("c4z", T=8192, H=4096, E=128, K=6, I=1408, S=0, block_m=128, seed=0,
+                     routing="zipf"),
     # Decode with 16 experts forced empty by a -10 selection bias (empty-group skipping).
     "c5e": MoEConfig("c5e", T=256, H=4096, E=128, K=6, I=1408, S=2, block_m=16, seed=7,
                      routing="router", sel_bias="forced_empty",
@@ -258,6 +262,22 @@ def uniform_logits(cfg: MoEConfig) -> np.ndarray:
     lo_sel = np.where(mask, v, np.inf).min(axis=1)
     hi_rest = np.where(mask, -np.inf, v).max(axis=1)
     assert np.all(lo_sel > hi_rest + 1.0), "uniform_logits: assignment margin too small"
+    return v
+
+
+def skewed_logits(cfg: MoEConfig, skew: float = 1.1) -> np.ndarray:
+    """Router logits [T,E] float32 whose top-K experts are a Zipf(skew) routing (draw_topk_given
+    with the config's seed): N(0,1) noise plus +16 on the token's K chosen experts, as in
+    uniform_logits."""
+    idx = draw_topk_given(cfg.T, cfg.E, cfg.K, cfg.seed, skew)
+    v = _rng(cfg.seed, TAG_LOGITS).standard_normal((cfg.T, cfg.E), dtype=np.float32)
+    rows = np.arange(cfg.T)[:, None]
+    v[rows, idx] += np.float32(16.0)
+    mask = np.zeros_like(v, dtype=bool)
+    mask[rows, idx] = True
+    lo_sel = np.where(mask, v, np.inf).min(axis=1)
+    hi_rest = np.where(mask, -np.inf, v).max(axis=1)
+    assert np.all(lo_sel > hi_rest + 1.0), "skewed_logits: assignment margin too small"
     return v
 
 
