@@ -66,6 +66,7 @@ struct GemmArgs {
   int M, N, K, I;
   int block_m;
   int max_blk;         // tall tiles: at most this many 128-row blocks per tile (2 or 3)
+  int tile_chunk;      // tall tiles: consecutive row tiles dealt to one XCD at a time (1..8)
   int n_tiles_n, n_tiles_m;
   int G;
   const int32_t* tile_group;
@@ -1360,6 +1361,25 @@ template <int ROWS> struct Tall8 {
   typedef Tile8<ROWS, kTall8BN, 4, 2, early ? 12 : 4, early ? 12 : 8> type;
 };
 
+// Position pos of the dealt order of n row tiles in chunks of q: chunks c = y, y + 8, ... for
+// y = 0..7 in turn, rows cq .. cq + q - 1 of each (the last chunk, the only partial one, is the
+// last of its class).
+__device__ __forceinline__ int dealt_row_tile(int pos, int n, int q) {
+  const int nch = (n + q - 1) / q, last = n - (nch - 1) * q;
+  int base = 0;
+#pragma unroll
+  for (int y = 0; y < kNumXcd; ++y) {
+    const int cnt = y < nch ? (nch - 1 - y) / kNumXcd + 1 : 0;
+    const int rows = cnt * q - ((cnt > 0 && (nch - 1) % kNumXcd == y) ? q - last : 0);
+    if (pos < base + rows) {
+      const int o = pos - base;
+      return (y + kNumXcd * (o / q)) * q + o % q;
+    }
+    base += rows;
+  }
+  return n - 1;   // not reached for pos < n
+}
+
 // Row-grouped kinds with block_m a multiple of 128: every segment is cut into
 // ceil(blocks / max_blk) tiles of whole 128-row blocks, as even as they come (the first `extra`
 // tiles one block taller), so no tile is taller than max_blk blocks.
@@ -1387,19 +1407,20 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   }
   __syncthreads();
   const int64_t n_tiles = pref[G];
-  // Row tiles are dealt to the XCDs in turn (hardware places workgroup b on XCD b % 8): XCD x
-  // takes row tiles x, x + 8, x + 16, ..., each with all its column tiles in a row, so the tiles
-  // that share a row tile's activation panel share that XCD's L2. Dealt in turn rather than in
-  // contiguous ranges, every XCD gets its share of the tall and the short tiles: with skewed
-  // routing the segments shrink along the group order, and equal-length ranges would give one
-  // XCD the many one-block tiles of the rare experts and another the three-block tiles of the
-  // popular ones.
-  const int64_t k = blockIdx.x / kNumXcd;
-  const int64_t L = (int64_t)(blockIdx.x % kNumXcd) + kNumXcd * (k / p.n_tiles_n);
+  // Each XCD (hardware places workgroup b on XCD b % 8) walks an equal contiguous range of the
+  // tiles taken in a dealt order of the row tiles, each row tile with all its column tiles in a
+  // row (so the tiles that share its activation panel share that XCD's L2). The dealt order lists
+  // chunks of Q = tile_chunk consecutive row tiles (which share a weight panel) class by class:
+  // chunks 0, 8, 16, ..., then chunks 1, 9, 17, ..., and so on. Every XCD thus gets about one
+  // class, a sample of the whole group order: with skewed routing the segments shrink along that
+  // order, and ranges of it would give one XCD the one-block tiles of the rare experts and another
+  // the three-block tiles of the popular ones. The ranges are cut by tile count, not at row-tile
+  // boundaries, so a few row tiles with many column tiles (a dense layer) still split evenly.
+  const int64_t L = xcd_remap(blockIdx.x, n_tiles * p.n_tiles_n);
   int g = 0, ti = 0, nt = 0;
-  if (L < n_tiles) {
-    ti = (int)L;
-    nt = (int)(k % p.n_tiles_n);
+  if (L >= 0) {
+    ti = dealt_row_tile((int)(L / p.n_tiles_n), (int)n_tiles, p.tile_chunk);
+    nt = (int)(L % p.n_tiles_n);
     int lo = 0, hi = G - 1;   // group of tile ti: largest g with pref[g] <= ti
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -1409,7 +1430,7 @@ __global__ __launch_bounds__(kThreads8, 1) void ggemm_tall8_kernel(GemmArgs p) {
   }
   const int t0 = pref[g], ntg = pref[g + 1] - t0;
   __syncthreads();   // pref is dead from here on: the DMA ring may overwrite it
-  if (L >= n_tiles) return;
+  if (L < 0) return;
   const int nb = (p.seg[g + 1] - p.seg[g]) / kTallBlk;
   const int local = ti - t0, base = nb / ntg, extra = nb % ntg;
   const int blk0 = local * base + min(local, extra), nblk = base + (local < extra ? 1 : 0);
@@ -1677,6 +1698,22 @@ int tall_max_blk(int64_t rows, int G, int n_tiles_n) {
   return cost(2) < 0.9 * cost(kTallMaxBlk) ? 2 : kTallMaxBlk;
 }
 
+// Row tiles of one segment share its weight panel, so the tall kernels' dealt order keeps chunks
+// of Q consecutive row tiles together: Q is the row tiles of an even split's segment (rows / G,
+// whole blocks, at most max_blk a tile), a power of two up to 8, and at most an eighth of all the
+// row tiles. Uniform 384-row segments take 1; one GPU's share under 8-way expert parallelism
+// (3072-row segments) 8, which keeps each expert on one XCD; the skewed layer (about 8 blocks a
+// segment) 2; a dense layer of 8192 rows 2 (22 row tiles) or 4 (32).
+int tall_tile_chunk(int64_t rows, int G, int max_blk) {
+  if (rows <= 0 || G <= 0) return 1;
+  const int64_t nb = (rows + (int64_t)G * kTallBlk - 1) / ((int64_t)G * kTallBlk);   // >= 1
+  const int64_t per_g = (nb + max_blk - 1) / max_blk;
+  const int64_t cap = per_g * G / kNumXcd;
+  int q = 1;
+  while (q < 8 && 2 * q <= per_g && 2 * q <= cap) q *= 2;
+  return q;
+}
+
 // Row-grouped kinds: tall tiles for block_m % 128 == 0, 64-row tiles for block_m == 64, the
 // register-staged engine for 16 and 32.
 // *rows_copied (if given) tells whether the launch writes a.out3 (the gathered gate/up product
@@ -1692,8 +1729,8 @@ hipError_t launch_rows(GemmArgs a, int64_t mcap, int64_t rows, hipStream_t st,
     a.max_blk = tall_max_blk(rows, a.G, a.n_tiles_n);
     // sum over groups of ceil(nb_g / mb) <= (sum nb_g + (mb - 1) G) / mb, sum nb_g <= mcap / 128
     const int64_t tiles = (mcap / kTallBlk + (a.max_blk - 1) * (int64_t)a.G) / a.max_blk + 1;
-    // every XCD gets ceil(tiles / 8) row tiles' worth of workgroups (see the kernel's mapping)
-    const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * a.n_tiles_n * kNumXcd;
+    a.tile_chunk = tall_tile_chunk(rows, a.G, a.max_blk);
+    const int64_t grid = (tiles * a.n_tiles_n + kNumXcd - 1) / kNumXcd * kNumXcd;
     if constexpr (KIND == kFwdGateUp) {
       if (a.a_rows) {
         // each of a row tile's n_tiles_n workgroups copies every n_tiles_n-th row of its stages,
