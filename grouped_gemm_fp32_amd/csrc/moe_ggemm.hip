@@ -12,7 +12,8 @@
 //   - four wavefronts with register-staged operands, 16- or 32-row tiles, for block_m 16 and 32.
 // The first two stage operands in LDS with the buffer->LDS DMA and read MN-major operands with
 // the transposing LDS read; the third loads through registers and transposes 8x8 in registers.
-// Tiles are mapped to XCDs so that tiles sharing an operand panel share an L2.
+// Tiles are mapped to XCDs so that tiles sharing an operand panel share an L2, and so that every
+// XCD gets an equal share of the work when segment lengths differ (skewed routing).
 //
 // Six kinds of tile share the engines:
 //   FwdGateUp   h = x_perm . W1[g]^T, fused a = silu(h_gate) * h_up (and h_save)
