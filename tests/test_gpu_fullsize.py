@@ -8,7 +8,7 @@ import torch
 import grouped_gemm_fp32_amd as M
 from oracle import moe_oracle as O
 from synth import (get_config, draw_probs, draw_x, draw_wg, draw_sel_bias, draw_logit_bias, draw_w1_all,
-                   draw_w2_all, draw_dy, uniform_topk, uniform_logits)
+                   draw_w2_all, draw_dy, uniform_topk, uniform_logits, skewed_logits)
 from tests.gpu_helpers import (DEV, log, bf16_dev, f32_dev, i32_dev, bits_host, vals_host, rel_l2,
                                assert_bf16_close, validated_routing)
 
@@ -95,13 +95,28 @@ def test_expert_parallel_share_forward_and_backward():
     _uniform_layer(get_config("ep8"), wgrad_groups=(5,), per_group=4)
 
 
-def _uniform_layer(cfg, wgrad_groups, per_group=3):
-    """Forward and backward at a uniformly routed full-size shape: exact routing and maps,
-    sampled rows through the FFN, the combine and the dgrad, and the whole weight gradients of
-    wgrad_groups (the oracle runs their full segments)."""
+def test_skewed_8192_tokens_forward_and_backward():
+    """The bench workload's shapes under Zipf(1.1)-skewed routing (bench.py --workload c4z: 58 to
+    6693 rows per expert). The most popular expert's weight-gradient tiles contract over more
+    than a hundred 64-row stages and the least popular's over one, so the persistent weight-gradient kernel cuts its XCD
+    ranges inside groups; both experts' whole weight gradients are checked."""
+    cfg = get_config("c4z")
+    idx, _ = O.select_topk(O.softmax_probs(skewed_logits(cfg)), None, cfg.K)
+    counts = O.expert_counts(idx, cfg.E)
+    hot, rare = int(np.argmax(counts)), int(np.argmin(counts))
+    log(f"skewed routing: expert {hot} has {counts[hot]} rows, expert {rare} {counts[rare]}")
+    _uniform_layer(cfg, wgrad_groups=(hot, rare), uniform=False)
+
+
+def _uniform_layer(cfg, wgrad_groups, per_group=3, uniform=True):
+    """Forward and backward at a full-size shape routed from logits that encode a given routing
+    (uniform, or skewed with uniform=False): exact routing and maps, sampled rows through the FFN,
+    the combine and the dgrad, and the whole weight gradients of wgrad_groups (the oracle runs
+    their full segments)."""
     log(f"full size: {cfg}")
     s = M.make_shape(cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.S, cfg.block_m)
-    x, dy, logits = draw_x(cfg), draw_dy(cfg), uniform_logits(cfg)
+    x, dy = draw_x(cfg), draw_dy(cfg)
+    logits = uniform_logits(cfg) if uniform else skewed_logits(cfg)
     w1, w2 = draw_w1_all(cfg), draw_w2_all(cfg)
     X, W1, W2 = bf16_dev(x), bf16_dev(w1), bf16_dev(w2)
     buf = _run_forward(cfg, s, X, W1, W2, dict(x=None, w_gate=None, logit_bias=None, sel_bias=None,
@@ -109,11 +124,14 @@ def _uniform_layer(cfg, wgrad_groups, per_group=3):
     # routing: the uniform assignment, exactly; weights from the oracle's own softmax
     probs = O.softmax_probs(logits)
     idx, w = O.select_topk(probs, None, cfg.K)
-    np.testing.assert_array_equal(np.sort(idx, 1), np.sort(uniform_topk(cfg.T, cfg.E, cfg.K), 1))
+    if uniform:
+        np.testing.assert_array_equal(np.sort(idx, 1), np.sort(uniform_topk(cfg.T, cfg.E, cfg.K), 1))
     np.testing.assert_array_equal(_np(buf["topk_idx"]), idx)
     np.testing.assert_allclose(_np(buf["topk_w"]), w, rtol=0, atol=1e-6)
     seg, rt, pos, total = _check_maps_exact(buf, idx, cfg)
-    np.testing.assert_array_equal(bits_host(buf["x_perm"][:total]), x[rt[:total]])
+    # the row copy, bit for bit: x[row_token[r]], zero bits on padding rows (skewed segments)
+    want = np.where((rt[:total] >= 0)[:, None], x[np.maximum(rt[:total], 0)], 0).astype(x.dtype)
+    np.testing.assert_array_equal(bits_host(buf["x_perm"][:total]), want)
     # sampled permuted rows through the expert FFN
     rng = np.random.default_rng(0)
     rows = _sample_rows(seg, rng, per_group=per_group)
@@ -147,10 +165,11 @@ def _uniform_layer(cfg, wgrad_groups, per_group=3):
     for t in range(cfg.T):
         for j in range(cfg.K):
             slot[pos[t, j]] = (t, j)
-    dyp_ref = np.zeros((len(rows), cfg.H))
+    dyp_ref = np.zeros((len(rows), cfg.H))   # zero on padding rows (no slot)
     for i, r in enumerate(rows):
-        t, j = slot[r]
-        dyp_ref[i] = O.round_bf16(np.float64(w[t, j]) * O.bf16_to_f64(dy[t]))
+        if r in slot:
+            t, j = slot[r]
+            dyp_ref[i] = O.round_bf16(np.float64(w[t, j]) * O.bf16_to_f64(dy[t]))
     groups = np.searchsorted(seg, rows, side="right") - 1
     dh_ref = np.zeros((len(rows), 2 * cfg.I))
     dx_ref = np.zeros((len(rows), cfg.H))
@@ -169,8 +188,9 @@ def _uniform_layer(cfg, wgrad_groups, per_group=3):
         hg, ag, yg = _oracle_rows(seg_rows, seg, rt, x, cfg, lambda q: w1[q], lambda q: w2[q])
         dyp = np.zeros((r1 - r0, cfg.H))
         for i, r in enumerate(seg_rows):
-            t, j = slot[r]
-            dyp[i] = O.round_bf16(np.float64(w[t, j]) * O.bf16_to_f64(dy[t]))
+            if r in slot:
+                t, j = slot[r]
+                dyp[i] = O.round_bf16(np.float64(w[t, j]) * O.bf16_to_f64(dy[t]))
         dhg, _ = O.expert_ffn_dgrad(dyp, O.round_bf16(hg), [0, r1 - r0], [w1[g]], [w2[g]], cfg.I)
         xg = O.gather_rows(x, rt[r0:r1])
         dw1, dw2 = O.expert_ffn_wgrad(xg, ag, dyp, dhg, [0, r1 - r0], cfg.I, cfg.H)
