@@ -226,6 +226,10 @@ def _compare_layer(buf, f, b):
     # one wave of tiles, so the host caps tiles at two 128-row blocks: the shared expert's 9
     # blocks split 2+2+2+2+1, a routed expert's 7 blocks 2+2+2+1
     (1100, 256, 4, 2, 128, 1, 128, (2,)),
+    # tall tiles dealt to the XCDs in chunks of 4 row tiles (segments of about 6 blocks, two-block
+    # tiles), skewed segments and a shared expert: 33 and 43 row tiles, a partial last chunk
+    (1536, 256, 8, 4, 128, 1, 128, ()),
+    (2000, 256, 8, 4, 128, 1, 128, ()),
     # a dense SwiGLU FFN as one group (E = K = 1): one segment of every token, many row tiles
     (1000, 512, 1, 1, 1024, 0, 128, ()),
     (777, 256, 1, 1, 320, 0, 64, ()),
