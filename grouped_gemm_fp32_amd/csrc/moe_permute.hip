@@ -14,6 +14,9 @@
 //   3. scatter: per token block, a [E][TB/32] bit mask of "token routed to e" gives each slot its
 //               stable rank (popcounts), hence pos[t,j] and row_token
 //   4. gather:  x_perm[r] = x[row_token[r]] or 0, 16-byte vector copies, rows < total_rows.
+// A batch of one token block (at most 256 tokens: decode) runs steps 1-3 in a single workgroup
+// (perm_small_kernel): the block bases are all zero, so it needs no workspace and saves three
+// launches.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -182,6 +185,99 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
   }
 }
 
+// Steps 1-3 for a batch of one token block (T <= 256), in one workgroup, with the same results as
+// the three kernels above: per-expert slot counts (every slot counted, as perm_hist_kernel does),
+// the padded prefix sum, tile_group, the padding rows cleared, then each slot's stable rank from
+// the [E][8] bit mask of its expert's tokens.
+constexpr int kSmallPermThreads = 1024;
+constexpr int kSmallPermT = 256;
+
+__global__ __launch_bounds__(kSmallPermThreads) void perm_small_kernel(
+    int T, int K, int E, int S, int B, int64_t mcap, const int32_t* __restrict__ idx,
+    int32_t* __restrict__ seg_offsets, int32_t* __restrict__ tile_group,
+    int32_t* __restrict__ total_rows, int32_t* __restrict__ row_token, int32_t* __restrict__ pos) {
+  constexpr int W = kSmallPermT / 32;   // mask words per expert
+  __shared__ int cnt[256];              // E <= 256
+  __shared__ int seg[256 + 4 + 1];      // G + 1 <= 261
+  __shared__ uint32_t mask[256 * W];
+  __shared__ int pref[256 * W];
+  const int tid = threadIdx.x;
+  const int G = E + S, n = T * K;
+  for (int i = tid; i < E * W; i += kSmallPermThreads) mask[i] = 0u;
+  for (int e = tid; e < E; e += kSmallPermThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kSmallPermThreads) {
+    const int t = i / K, e = idx[i];
+    if (e >= 0 && e < E) {
+      atomicAdd(&cnt[e], 1);
+      atomicOr(&mask[e * W + (t >> 5)], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kSmallPermThreads) {
+    int run = 0;
+    for (int w = 0; w < W; ++w) {
+      pref[e * W + w] = run;
+      run += __popc(mask[e * W + w]);
+    }
+  }
+  // padded group sizes, exclusive prefix sum by the first wavefront (shared groups last, T rows)
+  if (tid < 64) {
+    int run = 0;
+    for (int base = 0; base < G; base += 64) {
+      const int g = base + tid;
+      const int c = g < E ? cnt[g] : T;
+      const int padded = g < G ? (c + B - 1) / B * B : 0;
+      int x = padded;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (tid >= o) x += y;
+      }
+      if (g < G) seg[g] = run + x - padded;
+      run += __shfl(x, 63, 64);
+    }
+    if (tid == 0) {
+      seg[G] = run;
+      total_rows[0] = run;
+    }
+  }
+  __syncthreads();
+  const int total = seg[G];
+  for (int g = tid; g <= G; g += kSmallPermThreads) seg_offsets[g] = seg[g];
+  const int64_t nt = mcap / B;
+  for (int64_t i = tid; i < nt; i += kSmallPermThreads) {
+    const int64_t r = i * B;
+    int g = -1;
+    if (r < total) {
+      int lo = 0, hi = G - 1;   // largest g with seg[g] <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seg[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      g = lo;
+    }
+    tile_group[i] = g;
+  }
+  for (int64_t r = tid; r < mcap && r < total; r += kSmallPermThreads) row_token[r] = -1;
+  __syncthreads();   // the clears are ordered before the scatter's writes of the same rows
+  for (int i = tid; i < n; i += kSmallPermThreads) {
+    const int t = i / K, e = idx[i];
+    if (e < 0 || e >= E) {   // out of range (excluded by the contract): no row, pos = -1
+      pos[i] = -1;
+      continue;
+    }
+    const int w = t >> 5;
+    const int r = seg[e] + pref[e * W + w] + __popc(mask[e * W + w] & ((1u << (t & 31)) - 1u));
+    pos[i] = r;
+    row_token[r] = t;
+  }
+  for (int i = tid; i < S * T; i += kSmallPermThreads) {
+    const int sh = i / T, t = i % T;
+    row_token[seg[E + sh] + t] = t;
+  }
+}
+
 // One wavefront per row: x_perm[r] = x[row_token[r]] (or 0), 16 B per lane per step.
 constexpr int kGatherU = 8;   // 16-byte chunks per lane per batch (a 4096-wide row in one batch)
 
@@ -227,6 +323,13 @@ hipError_t launch_permute(const moe_shape_t& s, int64_t mcap, const int32_t* top
   const int TB = permute_token_block(s.T);
   const int nblk = (int)permute_num_blocks(s.T);
   const int G = s.E + s.S;
+  if (s.T <= kSmallPermT) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(kSmallPermThreads), 0, st, s.T, s.K, s.E,
+                       s.S, s.block_m, mcap, topk_idx, seg_offsets, tile_group, total_rows,
+                       row_token, pos);
+    if (x) return launch_gather_rows(s, mcap, total_rows, row_token, x, x_perm, st);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(perm_hist_kernel, dim3(nblk), dim3(kThreads), 0, st, s.T, s.K, s.E, TB,
                      topk_idx, ws);
   const size_t seg_lds = sizeof(int) * ((size_t)nblk * s.E + (G + 1) + s.E);

@@ -130,7 +130,9 @@ def _gpu_permute(s, idx, x_bits):
 @pytest.mark.parametrize("T,H,E,K,S,B,empty", [
     (64, 256, 8, 2, 1, 16, ()), (333, 256, 16, 4, 2, 32, (3, 9)), (1000, 128, 128, 6, 2, 128, ()),
     (4099, 128, 64, 8, 1, 64, tuple(range(0, 64, 5))), (257, 256, 256, 8, 4, 256, ()),
-    (70000, 128, 128, 6, 2, 16, ()), (5, 128, 4, 4, 0, 16, ())])
+    (70000, 128, 128, 6, 2, 16, ()), (5, 128, 4, 4, 0, 16, ()),
+    # the largest batch of one token block (the single-workgroup permutation) at the widest shape
+    (256, 128, 256, 8, 4, 16, (1, 200))])
 def test_permute_bitexact(T, H, E, K, S, B, empty):
     log(f"permute T={T} E={E} K={K} S={S} B={B}")
     idx = draw_topk_given(T, E, K, seed=T, forced_empty=empty)
