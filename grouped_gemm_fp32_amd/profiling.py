@@ -69,6 +69,7 @@ PART_OF = {
     "fill_i32_kernel": "route (count clear)", "count_kernel": "route (expert counts)",
     "count_kernel<false>": "route (expert counts)", "count_kernel<true>": "route (expert counts)",
     "perm_clear_rows_kernel": "permute (maps)",
+    "perm_small_kernel": "permute (segments and maps, one workgroup)",
     "perm_hist_kernel": "permute (segments)", "perm_segment_kernel": "permute (segments)",
     "perm_scatter_kernel": "permute (maps)", "zero_pad_rows_kernel": "combine_bwd (padding rows)",
     "ggemm_kernel<0,16,256,16,1>": "fwd_gateup (16-row tiles)",
